@@ -1,0 +1,228 @@
+"""Pins of the fp64 oracle's forward pass (CPU only).
+
+The pages print no attention values, so the oracle is pinned by mathematics:
+pure-Python brute force on tiny inputs, closed forms, and the exactness of the
+ring decomposition across all ranks.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synthetic import CONFIGS, make_workload
+from tests._brute import brute_attention
+
+
+def _tolist(x):
+    return np.asarray(x, dtype=np.float64).tolist()
+
+
+def _case(rng, B, S, Hq, Hkv, d, packed):
+    q = rng.standard_normal((B, S, Hq, d))
+    k = rng.standard_normal((B, S, Hkv, d))
+    v = rng.standard_normal((B, S, Hkv, d))
+    if packed:
+        pos = []
+        for _ in range(B):
+            row, cur = [], 0
+            while len(row) < S:
+                n = int(rng.integers(1, max(2, S // 2) + 1))
+                row.extend(range(n))
+            pos.append(row[:S])
+        pos = np.asarray(pos, dtype=np.int32)
+    else:
+        pos = np.tile(np.arange(S, dtype=np.int32), (B, 1))
+    return q, k, v, pos
+
+
+TINY = [
+    # (S, CP, Hq, Hkv, d)
+    (1, 1, 1, 1, 1),
+    (2, 2, 1, 1, 4),
+    (3, 1, 2, 1, 3),
+    (5, 1, 4, 2, 4),
+    (8, 4, 4, 2, 4),
+    (8, 2, 1, 1, 8),
+    (12, 4, 2, 2, 1),
+    (17, 1, 4, 4, 2),
+]
+
+
+@pytest.mark.parametrize("S,CP,Hq,Hkv,d", TINY)
+@pytest.mark.parametrize("mask", ["none", "causal", "packed"])
+def test_ring_forward_matches_brute_force(S, CP, Hq, Hkv, d, mask):
+    rng = np.random.default_rng(S * 1000 + CP * 100 + Hq * 10 + d)
+    B = 2 if S <= 8 else 1
+    q, k, v, pos = _case(rng, B, S, Hq, Hkv, d, mask == "packed")
+    causal = mask != "none"
+    seg = oracle.segment_ids(pos) if mask == "packed" else None
+    scale = 1.0 / math.sqrt(d)
+    C = S // CP
+    for r in range(CP):
+        q_loc = q[:, r * C:(r + 1) * C]
+        kc = [k[:, c * C:(c + 1) * C] for c in range(CP)]
+        vc = [v[:, c * C:(c + 1) * C] for c in range(CP)]
+        o, lse = oracle.ring_forward(q_loc, kc, vc, r, CP, scale, causal, seg)
+        o_dir, lse_dir = oracle.attention_full(q_loc, k, v, r * C + np.arange(C), np.arange(S),
+                                               scale, causal,
+                                               None if seg is None else seg[:, r * C:(r + 1) * C],
+                                               seg)
+        for b in range(B):
+            sq = None if seg is None else seg[b, r * C:(r + 1) * C].tolist()
+            sk = None if seg is None else seg[b].tolist()
+            o_bf, lse_bf = brute_attention(_tolist(q_loc[b]), _tolist(k[b]), _tolist(v[b]),
+                                           list(range(r * C, (r + 1) * C)), list(range(S)),
+                                           scale, causal, sq, sk)
+            np.testing.assert_allclose(o[b], np.asarray(o_bf), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[b], np.asarray(lse_bf), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(o_dir[b], np.asarray(o_bf), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse_dir[b], np.asarray(lse_bf), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_partial_with_no_visible_key_is_merge_identity(causal):
+    """A chunk entirely in the queries' future gives O = 0, LSE = -inf exactly."""
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 4, 2, 4))
+    k = rng.standard_normal((1, 4, 1, 4))
+    v = rng.standard_normal((1, 4, 1, 4))
+    o, lse = oracle.attention_full(q, k, v, np.arange(4), 4 + np.arange(4), 0.5, True)
+    assert np.all(o == 0.0)
+    assert np.all(lse == -np.inf)
+
+
+def test_closed_form_identical_keys():
+    """All keys equal: every visible key gets the same score s_i, so O_i is the mean of
+    the visible values and LSE_i = s_i + ln(#visible)."""
+    rng = np.random.default_rng(3)
+    S, Hq, Hkv, d, CP = 24, 4, 2, 8, 4
+    C = S // CP
+    q = rng.standard_normal((1, S, Hq, d))
+    krow = rng.standard_normal((Hkv, d))
+    k = np.broadcast_to(krow, (1, S, Hkv, d)).copy()
+    v = rng.standard_normal((1, S, Hkv, d))
+    scale = 1 / math.sqrt(d)
+    for r in range(CP):
+        o, lse = oracle.ring_forward(q[:, r * C:(r + 1) * C], [k[:, c * C:(c + 1) * C] for c in range(CP)],
+                                     [v[:, c * C:(c + 1) * C] for c in range(CP)], r, CP, scale, True)
+        for i in range(C):
+            gi = r * C + i
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                s = scale * float(q[0, gi, h] @ krow[g])
+                np.testing.assert_allclose(o[0, i, h], v[0, :gi + 1, g].mean(axis=0), atol=1e-13)
+                assert abs(lse[0, h, i] - (s + math.log(gi + 1))) < 1e-12
+
+
+def test_closed_form_identical_values():
+    """All values equal to one vector: O is that vector whatever the weights."""
+    rng = np.random.default_rng(4)
+    S, Hq, Hkv, d = 16, 2, 1, 5
+    q = rng.standard_normal((1, S, Hq, d))
+    k = rng.standard_normal((1, S, Hkv, d))
+    vrow = rng.standard_normal(d)
+    v = np.broadcast_to(vrow, (1, S, Hkv, d)).copy()
+    o, _ = oracle.ring_forward(q[:, 12:16], [k[:, c * 4:(c + 1) * 4] for c in range(4)],
+                               [v[:, c * 4:(c + 1) * 4] for c in range(4)], 3, 4, 0.7, True)
+    np.testing.assert_allclose(o[0], np.broadcast_to(vrow, (4, Hq, d)), atol=1e-14)
+
+
+def test_single_token():
+    """S = 1: the only key is the query's own; O = V and LSE = scale q.k."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 2, 3))
+    k = rng.standard_normal((1, 1, 1, 3))
+    v = rng.standard_normal((1, 1, 1, 3))
+    o, lse = oracle.ring_forward(q, [k], [v], 0, 1, 0.3, True)
+    np.testing.assert_array_equal(o[0, 0], np.stack([v[0, 0, 0]] * 2))
+    for h in range(2):
+        assert abs(lse[0, h, 0] - 0.3 * float(q[0, 0, h] @ k[0, 0, 0])) < 1e-15
+
+
+def test_packed_sample_starts_attend_only_themselves_full_size():
+    """Packed 16K row, rank 2 of 4: a token with position 0 starts a sample, so under
+    the causal same-sample mask it sees only itself: O_i = V_i, LSE_i = scale q_i.k_i.
+    Pinned at the real size through the ring path (every chunk, every merge)."""
+    cfg = CONFIGS[4]
+    wl = make_workload(cfg)
+    seg = oracle.segment_ids(wl.position_ids)
+    C, r = cfg.C, cfg.rank
+    starts = np.nonzero(wl.position_ids[0, r * C:(r + 1) * C] == 0)[0]
+    assert starts.size >= 1
+    q_rows = wl.q_local[:, starts]
+    o = np.zeros((1, starts.size, cfg.Hq, cfg.d))
+    lse = np.full((1, cfg.Hq, starts.size), -np.inf)
+    for c in oracle.ring_schedule(r, cfg.CP):
+        oc, lc = oracle.attention_full(q_rows, wl.k_chunks[c], wl.v_chunks[c], r * C + starts,
+                                       c * C + np.arange(C), cfg.scale, True,
+                                       seg[:, r * C + starts], seg[:, c * C:(c + 1) * C])
+        o, lse = oracle.lse_merge(o, lse, oc, lc)
+    k_r, v_r = wl.k_chunks[r][0], wl.v_chunks[r][0]
+    for n, i in enumerate(starts):
+        for h in range(cfg.Hq):
+            g = h // (cfg.Hq // cfg.Hkv)
+            np.testing.assert_array_equal(o[0, n, h], v_r[i, g].astype(np.float64))
+            s = cfg.scale * float(q_rows[0, n, h].astype(np.float64) @ k_r[i, g].astype(np.float64))
+            assert abs(lse[0, h, n] - s) < 1e-12
+
+
+@pytest.mark.parametrize("mask", ["causal", "packed"])
+def test_all_ranks_reconstruct_full_attention(mask):
+    """Concatenating every rank's ring result gives attention over the whole row."""
+    rng = np.random.default_rng(11)
+    S, CP, Hq, Hkv, d = 64, 4, 4, 2, 8
+    q, k, v, pos = _case(rng, 1, S, Hq, Hkv, d, mask == "packed")
+    seg = oracle.segment_ids(pos) if mask == "packed" else None
+    C = S // CP
+    o_full, lse_full = oracle.attention_full(q, k, v, np.arange(S), np.arange(S), 0.35, True, seg, seg)
+    parts = [oracle.ring_forward(q[:, r * C:(r + 1) * C], [k[:, c * C:(c + 1) * C] for c in range(CP)],
+                                 [v[:, c * C:(c + 1) * C] for c in range(CP)], r, CP, 0.35, True, seg)
+             for r in range(CP)]
+    np.testing.assert_allclose(np.concatenate([p[0] for p in parts], axis=1), o_full, atol=1e-13)
+    np.testing.assert_allclose(np.concatenate([p[1] for p in parts], axis=2), lse_full, atol=1e-13)
+
+
+def test_lse_statistics_sanity():
+    """Not a pin: with N(0,1) inputs and scale 1/sqrt(d) the scores are ~N(0,1), so the
+    LSE of a row seeing n keys is close to ln n + 1/2."""
+    rng = np.random.default_rng(21)
+    S, d = 2048, 64
+    q = rng.standard_normal((1, 8, 1, d))
+    k = rng.standard_normal((1, S, 1, d))
+    v = rng.standard_normal((1, S, 1, d))
+    _, lse = oracle.attention_full(q, k, v, S - 1 - np.arange(8), np.arange(S), 1 / math.sqrt(d), True)
+    assert np.all(np.abs(lse - (math.log(S) + 0.5)) < 0.25)
+
+
+def test_ring_schedule_order():
+    assert oracle.ring_schedule(3, 4) == [3, 2, 1, 0]
+    assert oracle.ring_schedule(7, 8) == [7, 6, 5, 4, 3, 2, 1, 0]
+    assert oracle.ring_schedule(2, 4) == [2, 1, 0, 3]
+    for cp in (1, 2, 3, 8):
+        for r in range(cp):
+            assert sorted(oracle.ring_schedule(r, cp)) == list(range(cp))
+
+
+def test_live_pair_counts_closed_form():
+    """Causal pair count of rank r's share with contiguous chunks of C:
+    r*C^2 (earlier chunks, fully visible) + C(C+1)/2 (diagonal chunk)."""
+    for S, CP, r in [(1024, 4, 3), (8192, 4, 3), (64, 8, 0), (96, 3, 1)]:
+        C = S // CP
+        n = oracle.live_pairs(r * C + np.arange(C), np.arange(S), True)
+        assert n == r * C * C + C * (C + 1) // 2
+    # 64K share of rank 7 of 8 (closed form only; the mask count is the same formula)
+    C = 8192
+    assert 7 * C * C + C * (C + 1) // 2 == 503_320_576
+
+
+def test_mask_combinations_exhaustive_small():
+    """allowed_mask against a direct enumeration of the definition."""
+    q_idx = np.array([3, 4, 5, 6])
+    k_idx = np.arange(8)
+    seg = np.array([0, 0, 1, 1, 1, 2, 2, 2])
+    m = oracle.allowed_mask(q_idx, k_idx, True, seg[q_idx], seg)
+    for (a, i), (b, j) in itertools.product(enumerate(q_idx), enumerate(k_idx)):
+        assert m[a, b] == (j <= i and seg[j] == seg[i])
