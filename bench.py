@@ -1,0 +1,392 @@
+"""Benchmark: forward + backward of one context-parallel rank's share of ring attention.
+
+Workload: the 64K share — B=1, Hq=32, Hkv=8, d=128, total S=65536 split into CP=8
+contiguous chunks of 8192, rank 7 (8 ring steps, the diagonal chunk causal), bf16
+inputs ~ N(0,1) (synthetic, seeded), fp32 accumulation.  One step = the whole ring
+forward (8 fwd steps, 7 merges, final bf16 conversion) + the whole ring backward
+(delta preprocess, 8 bwd steps, including zeroing the gradient accumulators), with
+all inputs resident in HBM.
+
+Throughput counts ALGORITHMIC flops on live (unmasked) pairs only: 4*Hq*d per pair
+forward (QK^T and PV) and 10*Hq*d backward (QK^T recomputed, dP, dV, dK, dQ).
+
+Prints ONE JSON line (rank 0).  --gpus N with N > 1 exits: this build measures one
+GPU's share.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal ring-attn fwd+bwd TFLOP/s and % MFMA peak, 8K local Q × 64K ctx bf16"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+
+def live_pairs_causal(C: int, rank: int) -> int:
+    """Causal pairs of rank `rank` with contiguous chunks of C: rank*C^2 + C(C+1)/2."""
+    return rank * C * C + C * (C + 1) // 2
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on host cores")
+    p.add_argument("--no-extras", action="store_true", help="skip the packed/8K/workspace side measurements")
+    p.add_argument("--profile-copy", action="store_true",
+                   help="also run one plain 1 GiB device copy (calibrates HBM byte counters)")
+    p.add_argument("--only", choices=["fwd", "bwd", "all"], default="all",
+                   help="restrict the timed loop (for profiling a single kernel family)")
+    return p.parse_args()
+
+
+class Timer:
+    """Per-entry-point HIP event timing on the stream the kernels are launched on."""
+
+    def __init__(self, torch, enabled=True):
+        self.torch = torch
+        self.enabled = enabled
+        self.events = {}
+        self.pending = None
+
+    def begin(self):
+        if self.enabled:
+            e = self.torch.cuda.Event(enable_timing=True)
+            e.record()
+            self.pending = e
+
+    def hook(self, name, _i):
+        if not self.enabled:
+            return
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.events.setdefault(name, []).append((self.pending, e))
+        self.pending = e
+
+    def mean_ms(self, name):
+        pairs = self.events.get(name, [])
+        if not pairs:
+            return None
+        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+    def total_ms(self, name):
+        return sum(a.elapsed_time(b) for a, b in self.events.get(name, []))
+
+    def count(self, name):
+        return len(self.events.get(name, []))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the ring (one rank); --gpus {args.gpus} is not supported "
+              "in this build: run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import context_long_sequence_amd as ra
+    from synthetic import CONFIGS, METRIC_CONFIG, make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ra.load()
+    dev = torch.device("cuda:0")
+    cfg = METRIC_CONFIG
+    C, r, CP = cfg.C, cfg.rank, cfg.CP
+    pairs = live_pairs_causal(C, r)
+    f_fwd = 4.0 * cfg.Hq * cfg.d * pairs
+    f_bwd = 10.0 * cfg.Hq * cfg.d * pairs
+
+    wl = make_workload(cfg, q_chunks=[r])
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+
+    q = t(wl.q_local)
+    ks = [t(k) for k in wl.k_chunks]
+    vs = [t(v) for v in wl.v_chunks]
+    do = t(wl.do)
+    del wl
+    o = torch.empty_like(q)
+    lse = torch.empty((1, cfg.Hq, C), dtype=torch.float32, device=dev)
+    dq = torch.empty((1, C, cfg.Hq, cfg.d), dtype=torch.float32, device=dev)
+    dks = [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in ks]
+    dvs = [torch.empty(v.shape, dtype=torch.float32, device=dev) for v in vs]
+    torch.cuda.synchronize()
+    base_alloc = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    ws = ra.RingWorkspace(1, C, cfg.Hq, cfg.d, dev, backward=True)
+
+    def step(timer=None):
+        hook = timer.hook if timer else None
+        if timer:
+            timer.begin()
+        if args.only in ("fwd", "all"):
+            ra.ring_forward(q, ks, vs, r, CP, causal=True, out=o, lse=lse, workspace=ws, step_hook=hook)
+        if args.only in ("bwd", "all"):
+            dq.zero_()
+            for x in dks:
+                x.zero_()
+            for x in dvs:
+                x.zero_()
+            if hook:
+                hook("zero_grads", 0)
+            ra.ring_backward(q, ks, vs, o, lse, do, r, CP, causal=True, dq=dq, dk_chunks=dks, dv_chunks=dvs,
+                             delta=ws.delta, step_hook=hook)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    workspace_peak = torch.cuda.max_memory_allocated() - base_alloc
+
+    # Timed region: K whole steps.
+    timer = Timer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    flops = {"all": f_fwd + f_bwd, "fwd": f_fwd, "bwd": f_bwd}[args.only]
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    t_fwd_step = timer.mean_ms("fwd_step")
+    t_merge = timer.mean_ms("merge")
+    t_bwd_step = timer.mean_ms("bwd_step")
+    t_pre = timer.mean_ms("bwd_preprocess")
+    per_step_ms = {}
+    for name in ("fwd_step", "merge", "zero_grads", "bwd_preprocess", "bwd_step"):
+        if timer.count(name):
+            per_step_ms[name] = timer.total_ms(name) / args.steps
+
+    # Dominant entry point by time.
+    roofline = None
+    merge_bytes = 3 * (C * cfg.Hq * cfg.d * 4) + 3 * (cfg.Hq * C * 4)
+    if per_step_ms:
+        dom = max(("fwd_step", "bwd_step"), key=lambda n: per_step_ms.get(n, 0.0))
+        if dom == "bwd_step" and t_bwd_step:
+            achieved = f_bwd / CP / (t_bwd_step * 1e-3) / 1e12
+            roofline = {"kernel": "ring_attn_bwd_step (dkdv_kernel + dq_kernel)", "bound": "mfma",
+                        "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "avg_launch_ms": round(t_bwd_step, 4), "flop_per_launch": f_bwd / CP}
+        elif t_fwd_step:
+            achieved = f_fwd / CP / (t_fwd_step * 1e-3) / 1e12
+            roofline = {"kernel": "ring_attn_fwd_step (fwd_step_kernel)", "bound": "mfma",
+                        "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "avg_launch_ms": round(t_fwd_step, 4), "flop_per_launch": f_fwd / CP}
+
+    extra = {
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "live_pairs": pairs,
+        "algorithmic_flop": {"fwd": f_fwd, "bwd": f_bwd},
+        "per_step_ms": {k: round(v, 4) for k, v in per_step_ms.items()},
+        "timer_ms": {"host_wall_per_step": round(ms_per_step, 4)},
+    }
+    if t_fwd_step and t_merge and args.only in ("fwd", "all"):
+        fwd_ms = per_step_ms["fwd_step"] + per_step_ms.get("merge", 0.0)
+        extra["fwd_tflops"] = round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2)
+        extra["merge"] = {"bytes_per_call": merge_bytes, "avg_us": round(t_merge * 1e3, 2),
+                          "GB_per_s": round(merge_bytes / (t_merge * 1e-3) / 1e9, 1),
+                          "frac_of_hbm_peak": round(merge_bytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if t_bwd_step and args.only in ("bwd", "all"):
+        bwd_ms = per_step_ms["bwd_step"] + per_step_ms.get("bwd_preprocess", 0.0)
+        extra["bwd_tflops"] = round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2)
+        if t_pre:
+            pre_bytes = 2 * C * cfg.Hq * cfg.d * 2 + cfg.Hq * C * 4
+            extra["bwd_preprocess_GB_per_s"] = round(pre_bytes / (t_pre * 1e-3) / 1e9, 1)
+    extra["workspace"] = {"peak_bytes": int(workspace_peak), "ring_workspace_bytes": ws.nbytes(),
+                          "score_matrix_avoided_bytes": C * cfg.S * cfg.Hq * 4}
+
+    if not args.no_extras:
+        extra.update(side_measurements(torch, ra, np, dev, CONFIGS, make_workload))
+
+    if args.profile_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) Q/K/V/dO rounded to bf16 (no dataset)",
+        "config": {"workload": "64K-context causal ring-attention share, rank 7 of CP=8, fwd+bwd"
+                               + ("" if args.only == "all" else f" ({args.only} only)"),
+                   "global_batch": 1, "seq_len": cfg.S, "local_q": C, "cp": CP, "rank": r,
+                   "heads_q": cfg.Hq, "heads_kv": cfg.Hkv, "head_dim": cfg.d, "parallelism": "cp8 (one rank)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def packed_live_pairs(lengths, C, rank):
+    """Causal same-sample pairs of rank `rank`'s queries, from the packed sample lengths:
+    a query at global index i inside sample [s0, s1) sees the i - s0 + 1 keys s0..i."""
+    total = 0
+    s0 = 0
+    lo, hi = rank * C, (rank + 1) * C
+    for n in lengths:
+        s1 = s0 + int(n)
+        a, b = max(s0, lo), min(s1, hi)
+        if a < b:
+            # sum_{i=a}^{b-1} (i - s0 + 1)
+            total += (b - a) * (a - s0 + 1 + b - s0) // 2
+        s0 = s1
+    return total
+
+
+def side_measurements(torch, ra, np, dev, CONFIGS, make_workload):
+    """Forward TFLOP/s of the 8K and packed-16K shares, the segment-id kernel time, and
+    the peak workspace of one forward+backward at S = 16K..128K (CP=8, rank 7)."""
+    out = {}
+
+    def ev_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+
+    # 8K Llama-3-8B-shaped share (rank 3 of 4), forward
+    c2 = CONFIGS[2]
+    wl = make_workload(c2, q_chunks=[c2.rank])
+    q, ks, vs = bf(wl.q_local), [bf(k) for k in wl.k_chunks], [bf(v) for v in wl.v_chunks]
+    ws = ra.RingWorkspace(1, c2.C, c2.Hq, c2.d, dev)
+    ms = ev_ms(lambda: ra.ring_forward(q, ks, vs, c2.rank, c2.CP, causal=True, workspace=ws))
+    pairs = live_pairs_causal(c2.C, c2.rank)
+    out["fwd_8k_cp4_r3"] = {"ms": round(ms, 4), "tflops": round(4.0 * c2.Hq * c2.d * pairs / (ms * 1e-3) / 1e12, 2)}
+
+    # packed 16K share (rank 2 of 4): segment ids + forward + backward
+    c4 = CONFIGS[4].with_(backward=True)
+    wl = make_workload(c4, q_chunks=[c4.rank])
+    q, ks, vs = bf(wl.q_local), [bf(k) for k in wl.k_chunks], [bf(v) for v in wl.v_chunks]
+    do = bf(wl.do)
+    pos = torch.from_numpy(wl.position_ids).to(dev)
+    seg = torch.empty_like(pos)
+    seg_ms = ev_ms(lambda: ra.segment_mask_from_pos(pos, seg), reps=20)
+    ws = ra.RingWorkspace(1, c4.C, c4.Hq, c4.d, dev, backward=True)
+    o4 = torch.empty_like(q)
+    l4 = torch.empty((1, c4.Hq, c4.C), dtype=torch.float32, device=dev)
+    fms = ev_ms(lambda: ra.ring_forward(q, ks, vs, c4.rank, c4.CP, causal=True, seg_ids=seg, workspace=ws,
+                                         out=o4, lse=l4))
+    bms = ev_ms(lambda: ra.ring_backward(q, ks, vs, o4, l4, do, c4.rank, c4.CP, causal=True, seg_ids=seg,
+                                         delta=ws.delta))
+    pairs4 = packed_live_pairs(wl.lengths, c4.C, c4.rank)
+    out["packed_16k_cp4_r2"] = {
+        "live_pairs": pairs4, "frac_of_causal_pairs": round(pairs4 / live_pairs_causal(c4.C, c4.rank), 4),
+        "segment_ids_us": round(seg_ms * 1e3, 2),
+        "fwd_ms": round(fms, 4), "fwd_tflops": round(4.0 * c4.Hq * c4.d * pairs4 / (fms * 1e-3) / 1e12, 2),
+        "bwd_ms": round(bms, 4), "bwd_tflops": round(10.0 * c4.Hq * c4.d * pairs4 / (bms * 1e-3) / 1e12, 2)}
+    del q, ks, vs, do, ws, o4, l4
+
+    # workspace sweep: peak bytes beyond inputs/outputs for one fwd+bwd, CP=8, rank 7
+    sweep = []
+    for S in (16384, 32768, 65536, 131072):
+        C = S // 8
+        g = torch.Generator(device=dev)
+        g.manual_seed(S)
+        qs = torch.randn((1, C, 32, 128), generator=g, device=dev).to(torch.bfloat16)
+        kk = [torch.randn((1, C, 8, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(8)]
+        vv = [torch.randn((1, C, 8, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(8)]
+        dd = torch.randn((1, C, 32, 128), generator=g, device=dev).to(torch.bfloat16)
+        oo = torch.empty_like(qs)
+        ll = torch.empty((1, 32, C), dtype=torch.float32, device=dev)
+        dq = torch.zeros((1, C, 32, 128), dtype=torch.float32, device=dev)
+        dk = [torch.zeros((1, C, 8, 128), dtype=torch.float32, device=dev) for _ in range(8)]
+        dv = [torch.zeros((1, C, 8, 128), dtype=torch.float32, device=dev) for _ in range(8)]
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        ra.ring_forward(qs, kk, vv, 7, 8, causal=True, out=oo, lse=ll)
+        ra.ring_backward(qs, kk, vv, oo, ll, dd, 7, 8, causal=True, dq=dq, dk_chunks=dk, dv_chunks=dv)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        sweep.append({"S": S, "workspace_bytes": int(peak), "bytes_per_token": round(peak / S, 1),
+                      "score_matrix_bytes_avoided": C * S * 32 * 4})
+        del qs, kk, vv, dd, oo, ll, dq, dk, dv
+        torch.cuda.empty_cache()
+    out["workspace_sweep_cp8_r7"] = sweep
+    return out
+
+
+def cpu_baseline(cfg, wl=None):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload: forward
+    and backward of the last R query rows of the 64K share (each sees all 65536 keys),
+    all 32 heads.  Reported in the metric's unit on the sample's algorithmic flops."""
+    import numpy as np
+
+    import oracle
+    from synthetic import make_workload
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    if wl is None:
+        wl = make_workload(cfg, q_chunks=[cfg.rank])
+    C, r = cfg.C, cfg.rank
+    R = 128
+    rows = np.arange(C - R, C)
+    q_rows = wl.q_local[:, rows]
+    do_rows = wl.do[:, rows]
+    k_full, v_full = wl.k_full(), wl.v_full()
+    q_idx = r * C + rows
+    k_idx = np.arange(cfg.S)
+    t0 = time.perf_counter()
+    o_ref, l_ref = oracle.attention_full(q_rows, k_full, v_full, q_idx, k_idx, cfg.scale, True)
+    delta = oracle.bwd_delta(o_ref, do_rows)
+    oracle.attention_bwd_full(q_rows, k_full, v_full, do_rows, l_ref, delta, q_idx, k_idx, cfg.scale, True)
+    dt = time.perf_counter() - t0
+    pairs = int(np.sum(q_idx + 1))
+    flops = 14.0 * cfg.Hq * cfg.d * pairs
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle fwd+bwd of the last {R} query rows of the 64K share "
+                      f"(rank 7, all {cfg.Hq} heads, {cfg.S} keys each): {pairs} live pairs, "
+                      f"{flops:.3e} algorithmic flop in {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

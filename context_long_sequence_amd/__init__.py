@@ -1,0 +1,18 @@
+"""One context-parallel rank's share of ring attention on AMD Instinct MI355X (gfx950).
+
+The compute lives in the HIP library ``libringattn.so`` (C ABI in include/ringattn.h);
+this package is its ctypes binding plus the ring schedule simulated on one GPU.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    RingAttnError,
+    library_path,
+    load,
+    lse_merge,
+    ring_attn_bwd_preprocess,
+    ring_attn_bwd_step,
+    ring_attn_fwd_step,
+    segment_mask_from_pos,
+)
+from .ring import RingWorkspace, ring_backward, ring_forward, ring_schedule  # noqa: F401

@@ -1,0 +1,383 @@
+// ring_attn_fwd_step: one ring step of attention — the local query shard against
+// one KV chunk — on gfx950 MFMA.
+//
+// What is computed (per batch row b, query head h, local query i):
+//   s_ij = scale * q_i . k_j over the visible keys j of this chunk,
+//   O_i = sum_j softmax_j(s_ij) v_j,  LSE_i = ln sum_j exp(s_ij)
+// with O = 0, LSE = -inf for a row that sees no key of this chunk.  This is the
+// per-chunk partial result that the ring merges step by step (axolotl docs
+// "Sequence Parallelism", introduction and Implementation Details; aicassindra
+// "Transformer math: SP math", section on context parallelism).  The score
+// matrix only ever exists one 32x64 register tile at a time (archcrux,
+// "sequence-parallel long-context attention OOM").
+//
+// Work decomposition: one workgroup = 4 waves = 128 queries of one (b, h); each
+// wave owns 32 queries.  The workgroup walks the chunk in tiles of 64 keys that
+// are staged in LDS (K row-major, V transposed) and shared by the 4 waves.
+//
+// Register layout: scores are computed transposed, S^T = K Q^T, so that the
+// accumulator column — the lane — is the query: lane l and lane l+32 hold the
+// 32 keys of one query row between them, and the row max / row sum are
+// in-register reductions plus one exchange between the two half-waves.  K rows
+// are loaded in a permuted order so that register i of half h holds key 16h+i;
+// P then feeds the P.V MFMA (O^T = V^T P^T) straight from registers as its B
+// operand, and V^T is read from LDS as 16-byte rows.
+#include "ra_device.h"
+#include "ra_host.h"
+
+namespace ra {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // queries per workgroup
+constexpr int kBN = 64;           // keys per tile
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seg;  // [B, seg_len] or null
+  int64_t seg_len;
+  float* o;
+  float* lse;
+  int B, Sq, Sk, Hq, Hkv;
+  int64_t q_offset, kv_offset;
+  int causal;
+  float scale_log2;  // softmax_scale * log2(e)
+  int n_qtiles;
+};
+
+template <typename T, int D, bool kSeg>
+__global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a) {
+  using M = Mfma<T>;
+  constexpr int KPL = M::KPL;
+  constexpr int E = 16 / sizeof(T);              // elements per 16-byte chunk
+  constexpr int KPAD = 16 / sizeof(T);           // K row padding (16 bytes)
+  constexpr int VPAD = 16 / sizeof(T);           // V^T row padding (16 bytes)
+  constexpr int KP = D + KPAD;                   // K tile row pitch (elements)
+  constexpr int VP = kBN + VPAD;                 // V^T tile row pitch (elements)
+  constexpr int QSTEPS = D / (2 * KPL);          // MFMAs per 32x32 score block
+  constexpr int PSTEPS = 16 / KPL;               // MFMAs per 32-key block of P.V
+  constexpr int DB = D / 32;                     // 32-row blocks of O^T
+  constexpr int KCH = kBN * D / E;               // 16-byte chunks of a K tile
+  constexpr int VUNITS = (kBN / 2) * (D / E);    // (key pair, chunk) units of a V tile
+  static_assert(KCH % kThreads == 0 && VUNITS % kThreads == 0, "tile/threads mismatch");
+  constexpr int KLD = KCH / kThreads;
+  constexpr int VLD = VUNITS / kThreads;
+
+  __shared__ __attribute__((aligned(16))) T k_lds[kBN * KP];
+  __shared__ __attribute__((aligned(16))) T vt_lds[D * VP];
+  __shared__ int seg_lds[kBN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // Workgroup -> (b, kv head, q head within group, q tile).  Tiles of one KV head
+  // are kept together on one XCD; the heaviest (latest) query tiles go first.
+  const int n_wg = gridDim.x;
+  const int logical = xcd_logical_id(blockIdx.x, n_wg);
+  const int group = a.Hq / a.Hkv;
+  int rem = logical;
+  const int qt_rev = rem % a.n_qtiles;
+  rem /= a.n_qtiles;
+  const int hg = rem % group;
+  rem /= group;
+  const int g = rem % a.Hkv;
+  const int b = rem / a.Hkv;
+  const int qt = a.n_qtiles - 1 - qt_rev;
+  const int hq = g * group + hg;
+
+  const int q0 = qt * kBM;                        // first query of the workgroup
+  const int q_last = min(q0 + kBM, a.Sq) - 1;     // last valid query of the workgroup
+  const int qw = q0 + wave * 32;                  // first query of this wave
+  const int qi = qw + col;                        // this lane's query
+  const bool q_valid = qi < a.Sq;
+  const int64_t qg = a.q_offset + qi;             // global index of this lane's query
+
+  const T* qbase = static_cast<const T*>(a.q);
+  const T* kbase = static_cast<const T*>(a.k);
+  const T* vbase = static_cast<const T*>(a.v);
+  const int64_t q_row_stride = (int64_t)a.Hq * D;
+  const int64_t kv_row_stride = (int64_t)a.Hkv * D;
+
+  // ---- key range of this workgroup -------------------------------------------------
+  int n_keys = a.Sk;
+  if (a.causal) {
+    const int64_t last_visible = a.q_offset + q_last - a.kv_offset;  // local key index
+    n_keys = (int)max<int64_t>(0, min<int64_t>((int64_t)a.Sk, last_visible + 1));
+  }
+  int kt_begin = 0;
+  int kt_end = (n_keys + kBN - 1) / kBN;
+  int seg_q = 0, seg_q_lo = 0, seg_q_hi = 0;
+  const int32_t* seg_row = nullptr;
+  if constexpr (kSeg) {
+    seg_row = a.seg + (int64_t)b * a.seg_len;
+    seg_q_lo = seg_row[a.q_offset + q0];
+    seg_q_hi = seg_row[a.q_offset + q_last];
+    seg_q = q_valid ? seg_row[a.q_offset + qi] : seg_q_lo;
+    // Segment ids are nondecreasing along the row, so the tiles that share a
+    // segment with this query tile form one contiguous range.
+    const int32_t* seg_k = seg_row + a.kv_offset;
+    int first_live = kt_end, last_live = -1;
+    for (int base = 0; base < kt_end; base += 64) {
+      const int t = base + lane;
+      bool live = false;
+      if (t < kt_end) {
+        const int k_first = t * kBN;
+        const int k_last = min((t + 1) * kBN, a.Sk) - 1;
+        live = seg_k[k_last] >= seg_q_lo && seg_k[k_first] <= seg_q_hi;
+      }
+      const uint64_t mask = __ballot(live);
+      if (mask) {
+        first_live = min(first_live, base + (int)__builtin_ctzll(mask));
+        last_live = max(last_live, base + 63 - (int)__builtin_clzll(mask));
+      }
+    }
+    kt_begin = first_live;
+    kt_end = last_live + 1;
+  }
+
+  // ---- Q fragments in registers (B operand of S^T = K Q^T) -----------------------------
+  typename M::frag qf[QSTEPS];
+  {
+    const T* qrow = qbase + ((int64_t)b * a.Sq + (q_valid ? qi : 0)) * q_row_stride + (int64_t)hq * D;
+#pragma unroll
+    for (int s = 0; s < QSTEPS; ++s) {
+      qf[s] = M::load(qrow + s * 2 * KPL + KPL * half);
+      if (!q_valid) qf[s] = typename M::frag{};
+    }
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;  // running max of log2-scaled scores (shared by both halves)
+  float l_run = 0.0f;       // running sum of this half's 16 keys per block
+
+  // ---- global -> register staging of one K/V tile ----------------------------------
+  u32x4 kreg[KLD];
+  u32x4 vreg[VLD][2];
+  int sreg = 0;
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * kBN;
+#pragma unroll
+    for (int r = 0; r < KLD; ++r) {
+      const int c = tid + r * kThreads;
+      const int key = c / (D / E), ch = c % (D / E);
+      const int kj = k0 + key;
+      if (kj < a.Sk)
+        kreg[r] = *reinterpret_cast<const u32x4*>(kbase + ((int64_t)b * a.Sk + kj) * kv_row_stride +
+                                                  (int64_t)g * D + ch * E);
+      else
+        kreg[r] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < VLD; ++r) {
+      const int u = tid + r * kThreads;
+      const int kp = u % (kBN / 2), ch = u / (kBN / 2);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int kj = k0 + 2 * kp + e;
+        if (kj < a.Sk)
+          vreg[r][e] = *reinterpret_cast<const u32x4*>(vbase + ((int64_t)b * a.Sk + kj) * kv_row_stride +
+                                                       (int64_t)g * D + ch * E);
+        else
+          vreg[r][e] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if constexpr (kSeg) {
+      if (tid < kBN) {
+        const int kj = k0 + tid;
+        sreg = kj < a.Sk ? seg_row[a.kv_offset + kj] : INT32_MIN;
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int r = 0; r < KLD; ++r) {
+      const int c = tid + r * kThreads;
+      const int key = c / (D / E), ch = c % (D / E);
+      *reinterpret_cast<u32x4*>(&k_lds[key * KP + ch * E]) = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VLD; ++r) {
+      const int u = tid + r * kThreads;
+      const int kp = u % (kBN / 2), ch = u / (kBN / 2);
+      if constexpr (sizeof(T) == 2) {
+        // 8 d-values of keys 2kp and 2kp+1 -> 8 rows of V^T, one dword (key pair) each.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t x0 = vreg[r][0][j], x1 = vreg[r][1][j];
+          const uint32_t lo = (x0 & 0xFFFFu) | (x1 << 16);          // d = 2j
+          const uint32_t hi = (x0 >> 16) | (x1 & 0xFFFF0000u);      // d = 2j+1
+          *reinterpret_cast<uint32_t*>(&vt_lds[(ch * E + 2 * j) * VP + 2 * kp]) = lo;
+          *reinterpret_cast<uint32_t*>(&vt_lds[(ch * E + 2 * j + 1) * VP + 2 * kp]) = hi;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x2 pr = {u32_as_f32(vreg[r][0][j]), u32_as_f32(vreg[r][1][j])};
+          *reinterpret_cast<f32x2*>(&vt_lds[(ch * E + j) * VP + 2 * kp]) = pr;
+        }
+      }
+    }
+    if constexpr (kSeg) {
+      if (tid < kBN) seg_lds[tid] = sreg;
+    }
+  };
+
+  if (kt_begin < kt_end) load_tile(kt_begin);
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    __syncthreads();  // previous tile fully consumed
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < kt_end) load_tile(kt + 1);  // overlaps with the math below
+
+    const int k0 = kt * kBN;
+    // Does this wave need per-element masking on this tile?
+    bool partial = (k0 + kBN > a.Sk);
+    if (a.causal) partial |= (a.kv_offset + k0 + kBN - 1 > a.q_offset + qw);
+    if constexpr (kSeg) partial = true;  // element test is cheap next to the tile's MFMAs
+
+    // S^T for two 32-key blocks.
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+      const T* krow = &k_lds[(32 * kb + key_of_row(col)) * KP + KPL * half];
+#pragma unroll
+      for (int s = 0; s < QSTEPS; ++s) sacc[kb] = M::mma(M::load(krow + s * 2 * KPL), qf[s], sacc[kb]);
+    }
+
+    // Scale to log2 units, mask, and find the tile max of this query row.
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float t = sacc[kb][i] * a.scale_log2;
+        if (partial) {
+          const int kl = 32 * kb + 16 * half + i;  // key within the tile
+          const int kj = k0 + kl;
+          bool vis = kj < a.Sk;
+          if (a.causal) vis = vis && (a.kv_offset + kj <= qg);
+          if constexpr (kSeg) vis = vis && (seg_lds[kl] == seg_q);
+          t = vis ? t : -INFINITY;
+        }
+        sacc[kb][i] = t;
+        tmax = fmaxf(tmax, t);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = exp2_fast(m_run - m_use);
+    m_run = m_new;
+
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2_fast(sacc[kb][i] - m_use);
+        sacc[kb][i] = p;
+        psum += p;
+      }
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float pv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pv[i] = sacc[kb][i];
+#pragma unroll
+      for (int m = 0; m < PSTEPS; ++m) {
+        const typename M::frag pf = M::pack(&pv[m * KPL]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const T* vrow = &vt_lds[(32 * db + col) * VP + 32 * kb + 16 * half + KPL * m];
+          oacc[db] = M::mma(M::load(vrow), pf, oacc[db]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue ---------------------------------------------------------------------
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const bool live = l_tot > 0.0f;
+  const float inv = live ? 1.0f / l_tot : 0.0f;
+  if (q_valid) {
+    float* orow = a.o + ((int64_t)b * a.Sq + qi) * q_row_stride + (int64_t)hq * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v = {oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv, oacc[db][4 * r4 + 2] * inv,
+                   oacc[db][4 * r4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * half) = v;
+      }
+    }
+    if (half == 0)
+      a.lse[((int64_t)b * a.Hq + hq) * a.Sq + qi] = live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename T, int D>
+ra_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
+  const int64_t n_wg = (int64_t)args.B * args.Hq * args.n_qtiles;
+  if (n_wg > INT32_MAX) return fail(RA_ERR_INVALID_ARGUMENT, "too many workgroups");
+  if (args.seg != nullptr)
+    hipLaunchKernelGGL((fwd_step_kernel<T, D, true>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((fwd_step_kernel<T, D, false>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, args);
+  return check_launch("ring_attn_fwd_step");
+}
+
+}  // namespace
+}  // namespace ra
+
+extern "C" ra_status ring_attn_fwd_step(const ra_shape* s, const void* q, const void* k, const void* v,
+                                        const int32_t* seg_ids, int64_t seg_len, float* o_step,
+                                        float* lse_step, void* stream) {
+  using namespace ra;
+  ra_status st = validate_step(s, seg_ids, seg_len);
+  if (st != RA_OK) return st;
+  if (!q || !k || !v || !o_step || !lse_step)
+    return fail(RA_ERR_INVALID_ARGUMENT, "q, k, v, o_step and lse_step must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_step) || !aligned16(lse_step))
+    return fail(RA_ERR_INVALID_ARGUMENT, "q, k, v, o_step and lse_step must be 16-byte aligned");
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.seg = seg_ids;
+  a.seg_len = seg_len;
+  a.o = o_step;
+  a.lse = lse_step;
+  a.B = s->batch;
+  a.Sq = s->q_len;
+  a.Sk = s->kv_len;
+  a.Hq = s->heads_q;
+  a.Hkv = s->heads_kv;
+  a.q_offset = s->q_offset;
+  a.kv_offset = s->kv_offset;
+  a.causal = s->causal;
+  a.scale_log2 = s->softmax_scale * kLog2e;
+  a.n_qtiles = (s->q_len + kBM - 1) / kBM;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (s->dtype == RA_DTYPE_BF16) {
+    if (s->head_dim == 128) return launch_fwd<__bf16, 128>(a, hs);
+    return launch_fwd<__bf16, 64>(a, hs);
+  }
+  if (s->head_dim == 128) return launch_fwd<float, 128>(a, hs);
+  return launch_fwd<float, 64>(a, hs);
+}

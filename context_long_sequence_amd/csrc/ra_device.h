@@ -1,0 +1,112 @@
+// Device-side helpers shared by the ring-attention kernels (gfx950 / CDNA4).
+//
+// MFMA conventions used throughout (64-lane wavefront, lane l, half h = l / 32):
+//  * v_mfma_f32_32x32x16_bf16 D = A*B + C with A 32x16, B 16x32, D 32x32.
+//    A: lane l holds row (l % 32), k-slots 8h .. 8h+7 (8 bf16).
+//    B: lane l holds column (l % 32), k-slots 8h .. 8h+7.
+//    D: lane l holds column (l % 32), rows 8*(i/4) + 4h + (i%4) for i = 0..15.
+//  * v_mfma_f32_32x32x2_f32: the same with one k-slot (h) per lane.
+// The contraction index can be permuted freely as long as A and B agree; the
+// kernels use that to keep operands in the registers where they are produced.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row layout helper for 32x32 MFMA outputs: row index of accumulator register i
+// in a lane of half h.
+__device__ __forceinline__ int mfma32_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even conversion of 8 floats to bf16 (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                            float a5, float a6, float a7) {
+  f32x2 p0 = {a0, a1}, p1 = {a2, a3}, p2 = {a4, a5}, p3 = {a6, a7};
+  bf16x2 r0 = __builtin_convertvector(p0, bf16x2);
+  bf16x2 r1 = __builtin_convertvector(p1, bf16x2);
+  bf16x2 r2 = __builtin_convertvector(p2, bf16x2);
+  bf16x2 r3 = __builtin_convertvector(p3, bf16x2);
+  bf16x8 out = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+  return out;
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const void* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ void store_bf16x8(void* p, bf16x8 v) {
+  *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
+}
+
+// Reinterprets 32 bits as a float.  Takes the value (not a vector-element lvalue):
+// bit-casting an ext_vector element in place reads the wrong element with this
+// compiler, so callers always go through this by-value helper.
+__device__ __forceinline__ float u32_as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(x) << 16);
+}
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<__bf16> {
+  static constexpr int KPL = 8;  // contraction values per lane per instruction
+  using frag = bf16x8;
+  static __device__ __forceinline__ frag load(const __bf16* p) { return load_bf16x8(p); }
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) { return mfma_bf16(a, b, c); }
+  static __device__ __forceinline__ frag pack(const float* p) {
+    return to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+  }
+};
+
+template <>
+struct Mfma<float> {
+  static constexpr int KPL = 1;
+  using frag = float;
+  static __device__ __forceinline__ frag load(const float* p) { return *p; }
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) { return mfma_f32(a, b, c); }
+  static __device__ __forceinline__ frag pack(const float* p) { return p[0]; }
+};
+
+// Row of the K tile that feeds accumulator row r of a 32-key block, chosen so
+// that accumulator register i of half-wave h holds key 16h + i.
+__device__ __forceinline__ int key_of_row(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+// Workgroup -> XCD remap.  Consecutive workgroup ids are dispatched round-robin
+// over the 8 XCDs of an MI355X; this returns a logical id such that each XCD
+// receives one contiguous range of logical ids (so workgroups that share K/V
+// tiles share that XCD's L2).  A bijection on [0, n).
+__device__ __forceinline__ int xcd_logical_id(int w, int n) {
+  constexpr int kXcd = 8;
+  const int xcd = w % kXcd;
+  const int local = w / kXcd;
+  const int base = n / kXcd, rem = n % kXcd;
+  // XCD x owns base + (x < rem) ids; its range starts at x*base + min(x, rem).
+  return xcd * base + min(xcd, rem) + local;
+}
+
+}  // namespace ra

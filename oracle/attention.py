@@ -108,6 +108,8 @@ def attention_rows(q, k, v, q_idx, k_idx, scale, causal, seg_q=None, seg_k=None)
         mask = allowed_mask(q_idx[rows], k_idx, causal,
                             None if seg_q_arr is None else seg_q_arr[rows], seg_k)
         live = mask.any(axis=1)
+        if not live.any():
+            continue  # no row of this block sees any key: O = 0, LSE = -inf as initialised
         for h in range(Hq):
             g = h // group
             s = scale * (q[rows, h, :] @ k[:, g, :].T)
@@ -221,6 +223,8 @@ def attention_bwd_rows(q, k, v, do, lse, delta, q_idx, k_idx, scale, causal,
         rows = slice(r0, min(Nq, r0 + ROW_BLOCK))
         mask = allowed_mask(q_idx[rows], k_idx, causal,
                             None if seg_q_arr is None else seg_q_arr[rows], seg_k)
+        if not mask.any():
+            continue  # no visible pair in this block: no contribution
         for h in range(Hq):
             g = h // group
             s = scale * (q[rows, h, :] @ k[:, g, :].T)

@@ -1,0 +1,265 @@
+"""GPU parity of each C-ABI entry point against the fp64 oracle on small seeded inputs
+that span several tiles and ragged tails (sizes that are not tile multiples)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synthetic import bf16_round
+from tests.gpu_util import device, lib, lse_close, max_abs, rel_to_max, report, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _qkv(rng, B, Sq, Sk, Hq, Hkv, d, dtype):
+    q = rng.standard_normal((B, Sq, Hq, d), dtype=np.float32)
+    k = rng.standard_normal((B, Sk, Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((B, Sk, Hkv, d), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    return q, k, v
+
+
+def _packed_pos(rng, B, S, lo, hi, mid_start=False):
+    rows = []
+    for _ in range(B):
+        row = list(range(3, 3 + int(rng.integers(lo, hi)))) if mid_start else []
+        while len(row) < S:
+            row.extend(range(int(rng.integers(lo, hi + 1))))
+        rows.append(row[:S])
+    return np.asarray(rows, dtype=np.int32)
+
+
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+# ---- segment ids -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,S,lo,hi,mid", [(1, 16384, 512, 4096, False), (3, 5000, 1, 50, True),
+                                           (2, 1, 1, 1, False), (1, 100003, 1, 700, True),
+                                           (2, 4097, 4097, 4097, False)])
+def test_segment_mask_from_pos_bit_exact(B, S, lo, hi, mid):
+    ra = lib()
+    rng = np.random.default_rng(S + B)
+    pos = _packed_pos(rng, B, S, lo, hi, mid)
+    seg = torch.empty((B, S), dtype=torch.int32, device=device())
+    ra.segment_mask_from_pos(to_dev(pos, torch.int32), seg)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(seg.cpu().numpy(), oracle.segment_ids(pos))
+
+
+# ---- merge -----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,Sq,Hq,d", [(1, 300, 4, 128), (2, 77, 3, 64), (1, 5, 1, 4)])
+def test_lse_merge(B, Sq, Hq, d):
+    ra = lib()
+    rng = np.random.default_rng(Sq)
+    o1 = rng.standard_normal((B, Sq, Hq, d)).astype(np.float32)
+    o2 = rng.standard_normal((B, Sq, Hq, d)).astype(np.float32)
+    l1 = (rng.standard_normal((B, Hq, Sq)) * 4 + 9).astype(np.float32)
+    l2 = (rng.standard_normal((B, Hq, Sq)) * 4 + 9).astype(np.float32)
+    # some rows dead in one or both partials (their O is 0 by the step contract)
+    dead1 = rng.random((B, Hq, Sq)) < 0.2
+    dead2 = rng.random((B, Hq, Sq)) < 0.2
+    l1[dead1] = -np.inf
+    l2[dead2] = -np.inf
+    o1[np.transpose(dead1, (0, 2, 1))] = 0
+    o2[np.transpose(dead2, (0, 2, 1))] = 0
+    o_ref, l_ref = oracle.lse_merge(o1, l1, o2, l2)
+    oa, la = to_dev(o1, torch.float32), to_dev(l1, torch.float32)
+    out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=device())
+    ra.lse_merge(oa, la, to_dev(o2, torch.float32), to_dev(l2, torch.float32), o_out=out)
+    torch.cuda.synchronize()
+    err = max_abs(to_np(oa), o_ref)
+    lse_close(to_np(la), l_ref, 1e-5)
+    report("lse_merge", o_err=err)
+    assert err <= 1e-5
+    # bf16 output is the RNE rounding of the merged fp32 O
+    np.testing.assert_array_equal(out.float().cpu().numpy(), bf16_round(oa.cpu().numpy()))
+    # rows dead in both partials are untouched
+    both = np.transpose(dead1 & dead2, (0, 2, 1))
+    assert np.all(to_np(oa)[both] == 0)
+
+
+def test_lse_merge_with_dead_step_is_identity_bitwise():
+    ra = lib()
+    rng = np.random.default_rng(3)
+    o1 = rng.standard_normal((1, 64, 2, 128)).astype(np.float32)
+    l1 = rng.standard_normal((1, 2, 64)).astype(np.float32)
+    oa, la = to_dev(o1, torch.float32), to_dev(l1, torch.float32)
+    os_ = torch.zeros_like(oa)
+    ls = torch.full_like(la, -math.inf)
+    ra.lse_merge(oa, la, os_, ls)
+    torch.cuda.synchronize()
+    assert np.array_equal(oa.cpu().numpy(), o1) and np.array_equal(la.cpu().numpy(), l1)
+
+
+def test_lse_merge_convert_only():
+    ra = lib()
+    rng = np.random.default_rng(4)
+    o1 = rng.standard_normal((2, 33, 3, 64)).astype(np.float32)
+    oa = to_dev(o1, torch.float32)
+    la = torch.zeros((2, 3, 33), dtype=torch.float32, device=device())
+    out = torch.empty((2, 33, 3, 64), dtype=torch.bfloat16, device=device())
+    ra.lse_merge(oa, la, None, None, o_out=out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.float().cpu().numpy(), bf16_round(o1))
+
+
+# ---- preprocess ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_bwd_preprocess(dtype, d):
+    ra = lib()
+    rng = np.random.default_rng(d)
+    B, Sq, Hq = 2, 131, 3
+    o = rng.standard_normal((B, Sq, Hq, d), dtype=np.float32)
+    do = rng.standard_normal((B, Sq, Hq, d), dtype=np.float32)
+    if dtype == "bf16":
+        o, do = bf16_round(o), bf16_round(do)
+    delta = torch.empty((B, Hq, Sq), dtype=torch.float32, device=device())
+    ra.ring_attn_bwd_preprocess(to_dev(o, TD[dtype]), to_dev(do, TD[dtype]), delta)
+    torch.cuda.synchronize()
+    err = max_abs(delta.cpu().numpy(), oracle.bwd_delta(o, do))
+    assert err <= 1e-4 * math.sqrt(d)
+
+
+# ---- one forward step ----------------------------------------------------------------------
+
+STEP_CASES = [
+    # (dtype, B, Sq, Sk, Hq, Hkv, d, q_off, kv_off, causal, packed)
+    ("f32", 1, 256, 256, 1, 1, 64, 768, 512, True, False),
+    ("f32", 1, 256, 256, 1, 1, 64, 768, 768, True, False),
+    ("bf16", 1, 300, 200, 4, 2, 128, 500, 400, True, False),     # ragged, partly in the future
+    ("bf16", 2, 130, 190, 4, 1, 128, 0, 0, False, False),        # non-causal, GQA 4:1, B=2
+    ("bf16", 1, 257, 129, 2, 2, 64, 1000, 2000, True, False),    # chunk fully in the future
+    ("bf16", 1, 200, 333, 6, 3, 64, 333, 0, True, False),
+    ("f32", 2, 97, 150, 2, 1, 128, 150, 0, True, False),
+    ("bf16", 1, 384, 384, 4, 2, 128, 384, 384, True, True),      # packed, diagonal chunk
+    ("bf16", 2, 256, 320, 4, 4, 128, 640, 320, True, True),      # packed, earlier chunk
+    ("f32", 1, 160, 96, 2, 1, 64, 256, 0, False, True),          # packed, non-causal
+]
+
+
+def _step_case(case, seed):
+    dtype, B, Sq, Sk, Hq, Hkv, d, q_off, kv_off, causal, packed = case
+    rng = np.random.default_rng(seed)
+    q, k, v = _qkv(rng, B, Sq, Sk, Hq, Hkv, d, dtype)
+    S = max(q_off + Sq, kv_off + Sk)
+    seg = oracle.segment_ids(_packed_pos(rng, B, S, 20, 200)) if packed else None
+    return q, k, v, seg, S
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_fwd_step_partial(case):
+    ra = lib()
+    dtype, B, Sq, Sk, Hq, Hkv, d, q_off, kv_off, causal, packed = case
+    q, k, v, seg, S = _step_case(case, 17 + Sq + Sk)
+    scale = 1 / math.sqrt(d)
+    o_ref, l_ref = oracle.attention_full(q, k, v, q_off + np.arange(Sq), kv_off + np.arange(Sk), scale, causal,
+                                         None if seg is None else seg[:, q_off:q_off + Sq],
+                                         None if seg is None else seg[:, kv_off:kv_off + Sk])
+    o = torch.full((B, Sq, Hq, d), float("nan"), dtype=torch.float32, device=device())
+    lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=device())
+    ra.ring_attn_fwd_step(to_dev(q, TD[dtype]), to_dev(k, TD[dtype]), to_dev(v, TD[dtype]), o, lse,
+                          q_offset=q_off, kv_offset=kv_off, causal=causal, scale=scale,
+                          seg_ids=None if seg is None else to_dev(seg, torch.int32))
+    torch.cuda.synchronize()
+    on, ln = to_np(o), to_np(lse)
+    tol_o, tol_l = (1e-4, 1e-4) if dtype == "f32" else (2e-2, 1e-3)
+    err_o = max_abs(on, o_ref)
+    err_l = lse_close(ln, l_ref, tol_l)
+    report("fwd_step", case=case, o_err=err_o, lse_err=err_l, o_rel=rel_to_max(on, o_ref))
+    assert err_o <= tol_o
+    if dtype == "bf16":
+        assert rel_to_max(on, o_ref) <= 2e-2
+    # rows without a visible key are exactly the merge identity
+    dead = ~np.isfinite(l_ref)
+    assert np.all(on[np.transpose(dead, (0, 2, 1))] == 0)
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bwd_step(case):
+    """One backward step with the oracle's own final LSE/delta as inputs: dQ, dK, dV."""
+    ra = lib()
+    dtype, B, Sq, Sk, Hq, Hkv, d, q_off, kv_off, causal, packed = case
+    q, k, v, seg, S = _step_case(case, 91 + Sq + Sk)
+    rng = np.random.default_rng(5 + Sq)
+    do = rng.standard_normal((B, Sq, Hq, d), dtype=np.float32)
+    if dtype == "bf16":
+        do = bf16_round(do)
+    scale = 1 / math.sqrt(d)
+    # a "final" LSE from another key set so that rows are never empty: the chunk plus
+    # the query's own position (the diagonal key)
+    seg_q = None if seg is None else seg[:, q_off:q_off + Sq]
+    seg_k = None if seg is None else seg[:, kv_off:kv_off + Sk]
+    o_c, l_c = oracle.attention_full(q, k, v, q_off + np.arange(Sq), kv_off + np.arange(Sk), scale, causal,
+                                     seg_q, seg_k)
+    lse_fin = np.logaddexp(np.where(np.isfinite(l_c), l_c, -np.inf), rng.standard_normal(l_c.shape) + 2.0)
+    delta = rng.standard_normal((B, Hq, Sq)) * 0.1
+    dq_ref, dk_ref, dv_ref = oracle.attention_bwd_full(q, k, v, do, lse_fin, delta, q_off + np.arange(Sq),
+                                                       kv_off + np.arange(Sk), scale, causal, seg_q, seg_k)
+    # accumulators start non-zero to check the += contract
+    dq0 = rng.standard_normal((B, Sq, Hq, d)).astype(np.float32)
+    dk0 = rng.standard_normal((B, Sk, Hkv, d)).astype(np.float32)
+    dv0 = rng.standard_normal((B, Sk, Hkv, d)).astype(np.float32)
+    dq, dk, dv = to_dev(dq0, torch.float32), to_dev(dk0, torch.float32), to_dev(dv0, torch.float32)
+    ra.ring_attn_bwd_step(to_dev(q, TD[dtype]), to_dev(k, TD[dtype]), to_dev(v, TD[dtype]), to_dev(do, TD[dtype]),
+                          to_dev(lse_fin.astype(np.float32), torch.float32),
+                          to_dev(delta.astype(np.float32), torch.float32), dq, dk, dv,
+                          q_offset=q_off, kv_offset=kv_off, causal=causal, scale=scale,
+                          seg_ids=None if seg is None else to_dev(seg, torch.int32))
+    torch.cuda.synchronize()
+    tol = 1e-4 if dtype == "f32" else 3e-2
+    errs = {}
+    for name, got, g0, ref in (("dq", dq, dq0, dq_ref), ("dk", dk, dk0, dk_ref), ("dv", dv, dv0, dv_ref)):
+        inc = to_np(got) - g0
+        if np.max(np.abs(ref)) == 0:
+            errs[name] = max_abs(inc, ref)
+            assert errs[name] <= 1e-6
+        else:
+            errs[name] = rel_to_max(inc, ref)
+            assert errs[name] <= tol, (name, errs[name])
+    report("bwd_step", case=case, **errs)
+
+
+def test_fwd_step_is_bitwise_repeatable():
+    ra = lib()
+    rng = np.random.default_rng(1)
+    q, k, v = _qkv(rng, 1, 512, 512, 8, 2, 128, "bf16")
+    qd, kd, vd = to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16)
+    outs = []
+    for _ in range(3):
+        o = torch.empty((1, 512, 8, 128), dtype=torch.float32, device=device())
+        lse = torch.empty((1, 8, 512), dtype=torch.float32, device=device())
+        ra.ring_attn_fwd_step(qd, kd, vd, o, lse, q_offset=512, kv_offset=0, causal=True, scale=0.088)
+        outs.append((o.cpu().numpy(), lse.cpu().numpy()))
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
+
+
+def test_invalid_arguments_enqueue_nothing():
+    ra = lib()
+    q = torch.zeros((1, 64, 4, 96), dtype=torch.bfloat16, device=device())
+    k = torch.zeros((1, 64, 2, 96), dtype=torch.bfloat16, device=device())
+    o = torch.zeros((1, 64, 4, 96), dtype=torch.float32, device=device())
+    lse = torch.zeros((1, 4, 64), dtype=torch.float32, device=device())
+    with pytest.raises(ra.RingAttnError) as e:
+        ra.ring_attn_fwd_step(q, k, k, o, lse, q_offset=0, kv_offset=0, causal=True, scale=0.1)
+    assert e.value.status == 2  # RA_ERR_UNSUPPORTED: head_dim 96
+    q = torch.zeros((1, 64, 3, 64), dtype=torch.bfloat16, device=device())
+    k = torch.zeros((1, 64, 2, 64), dtype=torch.bfloat16, device=device())
+    o = torch.zeros((1, 64, 3, 64), dtype=torch.float32, device=device())
+    lse = torch.zeros((1, 3, 64), dtype=torch.float32, device=device())
+    with pytest.raises(ra.RingAttnError) as e:
+        ra.ring_attn_fwd_step(q, k, k, o, lse, q_offset=0, kv_offset=0, causal=True, scale=0.1)
+    assert e.value.status == 1  # Hq % Hkv != 0
+    seg = torch.zeros((1, 100), dtype=torch.int32, device=device())
+    k = torch.zeros((1, 64, 3, 64), dtype=torch.bfloat16, device=device())
+    with pytest.raises(ra.RingAttnError) as e:
+        ra.ring_attn_fwd_step(q, k, k, o, lse, q_offset=64, kv_offset=0, causal=True, scale=0.1, seg_ids=seg)
+    assert e.value.status == 1  # q range past seg_len
+    assert torch.all(o == 0) and torch.all(lse == 0)
