@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
   constexpr int KPL = M::KPL;
   constexpr int E = 16 / sizeof(T);
   constexpr int PAD = 16 / sizeof(T);
-  constexpr int BMQ = 32;                 // queries per tile
+  constexpr int BMQ = 64;                 // queries per tile (two 32-query MFMA blocks)
   constexpr int QP = D + PAD;             // row-major Q/dO pitch
   constexpr int TP = BMQ + PAD;           // transposed Q/dO pitch
   constexpr int QSTEPS = D / (2 * KPL);
@@ -248,44 +248,67 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
     if (a.causal) partial |= (a.kv_offset + kw + 31 > a.q_offset + q0);
     if constexpr (kSeg) partial = true;
 
-    // S = Q K^T and dP = dO V^T: lane = key, register i of half h = query 16h + i.
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
-    {
-      const T* qrow = &q_lds[key_of_row(col) * QP + KPL * half];
-      const T* drow = &do_lds[key_of_row(col) * QP + KPL * half];
+    auto tile = [&](auto mask_tag) {
+      constexpr bool kMask = decltype(mask_tag)::value;
 #pragma unroll
-      for (int s = 0; s < QSTEPS; ++s) {
-        sacc = M::mma(M::load(qrow + s * 2 * KPL), kf[s], sacc);
-        dpacc = M::mma(M::load(drow + s * 2 * KPL), vf[s], dpacc);
+      for (int qb = 0; qb < BMQ / 32; ++qb) {
+        // S = Q K^T and dP = dO V^T: lane = key, register i of half h = query 32qb + 16h + i.
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        {
+          const T* qrow = &q_lds[(32 * qb + key_of_row(col)) * QP + KPL * half];
+          typename M::frag f[QSTEPS];
+#pragma unroll
+          for (int s = 0; s < QSTEPS; ++s) f[s] = M::load(qrow + s * 2 * KPL);
+#pragma unroll
+          for (int s = 0; s < QSTEPS; ++s) sacc = M::mma(f[s], kf[s], sacc);
+        }
+        {
+          const T* drow = &do_lds[(32 * qb + key_of_row(col)) * QP + KPL * half];
+          typename M::frag f[QSTEPS];
+#pragma unroll
+          for (int s = 0; s < QSTEPS; ++s) f[s] = M::load(drow + s * 2 * KPL);
+#pragma unroll
+          for (int s = 0; s < QSTEPS; ++s) dpacc = M::mma(f[s], vf[s], dpacc);
+        }
+        float p[16], ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ql = 32 * qb + 16 * half + i;
+          float pi = exp2_fast(__builtin_fmaf(sacc[i], a.scale_log2, -lse_lds[ql]));
+          if constexpr (kMask) {
+            const int qi = q0 + ql;
+            bool vis = qi < a.Sq && k_valid;
+            if (a.causal) vis = vis && (kgl <= a.q_offset + qi);
+            if constexpr (kSeg) vis = vis && (segq_lds[ql] == seg_k);
+            pi = vis ? pi : 0.0f;
+          }
+          p[i] = pi;
+          ds[i] = pi * (dpacc[i] - dl_lds[ql]);
+        }
+        // dV += P^T dO, dK += dS^T Q (scale applied at the end).
+#pragma unroll
+        for (int m = 0; m < PSTEPS; ++m) {
+          typename M::frag dof_t[DB], qf_t[DB];
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int off = (32 * db + col) * TP + 32 * qb + 16 * half + KPL * m;
+            dof_t[db] = M::load(&dot_lds[off]);
+            qf_t[db] = M::load(&qt_lds[off]);
+          }
+          const typename M::frag pf = M::pack(&p[m * KPL]);
+          const typename M::frag sf = M::pack(&ds[m * KPL]);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dvacc[db] = M::mma(pf, dof_t[db], dvacc[db]);
+            dkacc[db] = M::mma(sf, qf_t[db], dkacc[db]);
+          }
+        }
       }
-    }
-    float p[16], ds[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ql = 16 * half + i;
-      float pi = exp2_fast(sacc[i] * a.scale_log2 - lse_lds[ql]);
-      if (partial) {
-        const int qi = q0 + ql;
-        bool vis = qi < a.Sq && k_valid;
-        if (a.causal) vis = vis && (kgl <= a.q_offset + qi);
-        if constexpr (kSeg) vis = vis && (segq_lds[ql] == seg_k);
-        pi = vis ? pi : 0.0f;
-      }
-      p[i] = pi;
-      ds[i] = pi * (dpacc[i] - dl_lds[ql]);
-    }
-    // dV += P^T dO, dK += dS^T Q (scale applied at the end).
-#pragma unroll
-    for (int m = 0; m < PSTEPS; ++m) {
-      const typename M::frag pf = M::pack(&p[m * KPL]);
-      const typename M::frag sf = M::pack(&ds[m * KPL]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int off = (32 * db + col) * TP + 16 * half + KPL * m;
-        dvacc[db] = M::mma(pf, M::load(&dot_lds[off]), dvacc[db]);
-        dkacc[db] = M::mma(sf, M::load(&qt_lds[off]), dkacc[db]);
-      }
-    }
+    };
+    if (partial)
+      tile(BoolTag<true>{});
+    else
+      tile(BoolTag<false>{});
   }
 
   // dK/dV accumulators: lane = d column, register i of half h = key row mfma32_row(i, h).
@@ -449,44 +472,65 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
     __syncthreads();
     if (t + 1 < kt_end) load_tile(t + 1);
     const int k0 = t * BN;
-    bool partial = (k0 + BN > a.Sk) || !q_valid;
+    // Wave-uniform (the two tile bodies contain MFMAs, which must not diverge).
+    bool partial = (k0 + BN > a.Sk) || (qw + 32 > a.Sq);
     if (a.causal) partial |= (a.kv_offset + k0 + BN - 1 > a.q_offset + qw);
     if constexpr (kSeg) partial = true;
 
+    auto tile = [&](auto mask_tag) {
+      constexpr bool kMask = decltype(mask_tag)::value;
 #pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk) {
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
-      const T* krow = &k_lds[(32 * kbk + key_of_row(col)) * KP + KPL * half];
-      const T* vrow = &v_lds[(32 * kbk + key_of_row(col)) * KP + KPL * half];
+      for (int kbk = 0; kbk < 2; ++kbk) {
+        const T* krow = &k_lds[(32 * kbk + key_of_row(col)) * KP + KPL * half];
+        const T* vrow = &v_lds[(32 * kbk + key_of_row(col)) * KP + KPL * half];
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        {
+          typename M::frag kf[QSTEPS];
 #pragma unroll
-      for (int s = 0; s < QSTEPS; ++s) {
-        sacc = M::mma(M::load(krow + s * 2 * KPL), qf[s], sacc);
-        dpacc = M::mma(M::load(vrow + s * 2 * KPL), dof[s], dpacc);
-      }
-      float ds[16];
+          for (int s = 0; s < QSTEPS; ++s) kf[s] = M::load(krow + s * 2 * KPL);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pi = exp2_fast(sacc[i] * a.scale_log2 - lse2);
-        if (partial) {
-          const int kl = 32 * kbk + 16 * half + i;
-          const int kj = k0 + kl;
-          bool vis = q_valid && kj < a.Sk;
-          if (a.causal) vis = vis && (a.kv_offset + kj <= qg);
-          if constexpr (kSeg) vis = vis && (segk_lds[kl] == seg_q);
-          pi = vis ? pi : 0.0f;
+          for (int s = 0; s < QSTEPS; ++s) sacc = M::mma(kf[s], qf[s], sacc);
         }
-        ds[i] = pi * (dpacc[i] - dl);
-      }
-      // dQ^T += K^T dS^T
+        {
+          typename M::frag vf[QSTEPS];
 #pragma unroll
-      for (int m = 0; m < PSTEPS; ++m) {
-        const typename M::frag sf = M::pack(&ds[m * KPL]);
+          for (int s = 0; s < QSTEPS; ++s) vf[s] = M::load(vrow + s * 2 * KPL);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dqacc[db] = M::mma(M::load(&kt_lds[(32 * db + col) * TP + 32 * kbk + 16 * half + KPL * m]), sf,
-                             dqacc[db]);
+          for (int s = 0; s < QSTEPS; ++s) dpacc = M::mma(vf[s], dof[s], dpacc);
+        }
+        typename M::frag ktf[PSTEPS][DB];
+#pragma unroll
+        for (int m = 0; m < PSTEPS; ++m)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            ktf[m][db] = M::load(&kt_lds[(32 * db + col) * TP + 32 * kbk + 16 * half + KPL * m]);
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pi = exp2_fast(__builtin_fmaf(sacc[i], a.scale_log2, -lse2));
+          if constexpr (kMask) {
+            const int kl = 32 * kbk + 16 * half + i;
+            const int kj = k0 + kl;
+            bool vis = q_valid && kj < a.Sk;
+            if (a.causal) vis = vis && (a.kv_offset + kj <= qg);
+            if constexpr (kSeg) vis = vis && (segk_lds[kl] == seg_q);
+            pi = vis ? pi : 0.0f;
+          }
+          ds[i] = pi * (dpacc[i] - dl);
+        }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int m = 0; m < PSTEPS; ++m) {
+          const typename M::frag sf = M::pack(&ds[m * KPL]);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) dqacc[db] = M::mma(ktf[m][db], sf, dqacc[db]);
+        }
       }
-    }
+    };
+    if (partial)
+      tile(BoolTag<true>{});
+    else
+      tile(BoolTag<false>{});
   }
 
   if (q_valid) {

@@ -32,6 +32,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // queries per workgroup
 constexpr int kBN = 64;           // keys per tile
+constexpr float kSlack = 8.0f;    // lazy-rescale threshold (log2 units)
 
 struct FwdArgs {
   const void* q;
@@ -239,76 +240,97 @@ __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a) {
     if (kt + 1 < kt_end) load_tile(kt + 1);  // overlaps with the math below
 
     const int k0 = kt * kBN;
-    // Does this wave need per-element masking on this tile?
+    // Does this wave need per-element masking on this tile?  (wave-uniform)
     bool partial = (k0 + kBN > a.Sk);
     if (a.causal) partial |= (a.kv_offset + k0 + kBN - 1 > a.q_offset + qw);
     if constexpr (kSeg) partial = true;  // element test is cheap next to the tile's MFMAs
 
-    // S^T for two 32-key blocks.
-    f32x16 sacc[2];
+    auto tile = [&](auto mask_tag) {
+      constexpr bool kMask = decltype(mask_tag)::value;
+      // S^T for two 32-key blocks; the 16-byte K operands are fetched as a batch.
+      f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      const T* krow = &k_lds[(32 * kb + key_of_row(col)) * KP + KPL * half];
+      for (int kb = 0; kb < 2; ++kb) {
+        const T* krow = &k_lds[(32 * kb + key_of_row(col)) * KP + KPL * half];
+        typename M::frag kf[QSTEPS];
 #pragma unroll
-      for (int s = 0; s < QSTEPS; ++s) sacc[kb] = M::mma(M::load(krow + s * 2 * KPL), qf[s], sacc[kb]);
-    }
-
-    // Scale to log2 units, mask, and find the tile max of this query row.
-    float tmax = -INFINITY;
+        for (int s = 0; s < QSTEPS; ++s) kf[s] = M::load(krow + s * 2 * KPL);
+        sacc[kb] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float t = sacc[kb][i] * a.scale_log2;
-        if (partial) {
-          const int kl = 32 * kb + 16 * half + i;  // key within the tile
-          const int kj = k0 + kl;
-          bool vis = kj < a.Sk;
-          if (a.causal) vis = vis && (a.kv_offset + kj <= qg);
-          if constexpr (kSeg) vis = vis && (seg_lds[kl] == seg_q);
-          t = vis ? t : -INFINITY;
-        }
-        sacc[kb][i] = t;
-        tmax = fmaxf(tmax, t);
+        for (int s = 0; s < QSTEPS; ++s) sacc[kb] = M::mma(kf[s], qf[s], sacc[kb]);
       }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    m_run = m_new;
 
-    float psum = 0.0f;
+      // Row max of the raw scores (the scale is positive, so it commutes with max).
+      float rmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2_fast(sacc[kb][i] - m_use);
-        sacc[kb][i] = p;
-        psum += p;
-      }
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float pv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pv[i] = sacc[kb][i];
-#pragma unroll
-      for (int m = 0; m < PSTEPS; ++m) {
-        const typename M::frag pf = M::pack(&pv[m * KPL]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const T* vrow = &vt_lds[(32 * db + col) * VP + 32 * kb + 16 * half + KPL * m];
-          oacc[db] = M::mma(M::load(vrow), pf, oacc[db]);
+        for (int i = 0; i < 16; ++i) {
+          float sv = sacc[kb][i];
+          if constexpr (kMask) {
+            const int kl = 32 * kb + 16 * half + i;  // key within the tile
+            const int kj = k0 + kl;
+            bool vis = kj < a.Sk;
+            if (a.causal) vis = vis && (a.kv_offset + kj <= qg);
+            if constexpr (kSeg) vis = vis && (seg_lds[kl] == seg_q);
+            sv = vis ? sv : -INFINITY;
+            sacc[kb][i] = sv;
+          }
+          rmax = fmaxf(rmax, sv);
         }
       }
-    }
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+      const float tmax = rmax * a.scale_log2;
+      // Lazy rescaling: the running max only moves when a row's max grows by more
+      // than kSlack (log2 units), so P stays <= 2^kSlack and most tiles skip the
+      // rescale of O entirely.  Both halves of a row see the same tmax and m_run.
+      const bool grow = tmax > m_run + kSlack;
+      if (__ballot(grow)) {
+        const float m_new = grow ? tmax : m_run;
+        const float alpha = grow ? exp2_fast(m_run - m_new) : 1.0f;  // 0 when m_run = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
+
+      float psum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = exp2_fast(__builtin_fmaf(sacc[kb][i], a.scale_log2, neg_m));
+          sacc[kb][i] = p;
+          psum += p;
+        }
+      }
+      l_run += psum;
+
+      // O^T += V^T P^T.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float pv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pv[i] = sacc[kb][i];
+        typename M::frag vf[PSTEPS][DB];
+#pragma unroll
+        for (int m = 0; m < PSTEPS; ++m)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            vf[m][db] = M::load(&vt_lds[(32 * db + col) * VP + 32 * kb + 16 * half + KPL * m]);
+#pragma unroll
+        for (int m = 0; m < PSTEPS; ++m) {
+          const typename M::frag pf = M::pack(&pv[m * KPL]);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] = M::mma(vf[m][db], pf, oacc[db]);
+        }
+      }
+    };
+    if (partial)
+      tile(BoolTag<true>{});
+    else
+      tile(BoolTag<false>{});
   }
 
   // ---- epilogue ---------------------------------------------------------------------
