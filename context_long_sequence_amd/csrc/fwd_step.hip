@@ -22,6 +22,8 @@
 // are loaded in a permuted order so that register i of half h holds key 16h+i;
 // P then feeds the P.V MFMA (O^T = V^T P^T) straight from registers as its B
 // operand, and V^T is read from LDS as 16-byte rows.
+#include <type_traits>
+
 #include "ra_device.h"
 #include "ra_host.h"
 
@@ -353,10 +355,314 @@ __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------------------------------
+// bf16, head_dim 128: the hot shape.  One workgroup = 4 waves x 64 queries (two
+// 32-query MFMA blocks per wave, so every K/V operand read from LDS feeds two
+// MFMAs).  Key tiles of 32 are prefetched into registers one step ahead and stored
+// into double-buffered, swizzled, row-major LDS tiles; V^T operands come from
+// transposing LDS reads, so V needs no transposition on the way in.  The loop is software-pipelined: the scores of tile t+1
+// are issued before the softmax of tile t, so the matrix cores work while the
+// vector ALUs do the softmax.
+// ------------------------------------------------------------------------------------
+#ifndef RA_FWD_QB
+#define RA_FWD_QB 1  // 32-query MFMA blocks per wave
+#endif
+#ifndef RA_FWD_PIPE
+#define RA_FWD_PIPE 1  // issue the scores of tile t+1 before the softmax of tile t
+#endif
+constexpr int kD128Waves = 4;
+constexpr int kD128Threads = 64 * kD128Waves;
+constexpr int kD128QB = RA_FWD_QB;
+constexpr int kD128QW = 32 * kD128QB;             // queries per wave
+constexpr int kD128BM = kD128QW * kD128Waves;     // queries per workgroup
+constexpr int kD128BN = 32;                       // keys per tile
+
+template <bool kSeg>
+__global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) {
+  constexpr int D = 128, BN = kD128BN, BM = kD128BM, QW = kD128QW, QB = kD128QB;
+  constexpr bool kPipe = RA_FWD_PIPE;
+  __shared__ __attribute__((aligned(1024))) __bf16 kbuf[2][BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 vbuf[2][BN * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int group = a.Hq / a.Hkv;
+  int rem = logical;
+  const int qt_rev = rem % a.n_qtiles;
+  rem /= a.n_qtiles;
+  const int hg = rem % group;
+  rem /= group;
+  const int g = rem % a.Hkv;
+  const int b = rem / a.Hkv;
+  const int qt = a.n_qtiles - 1 - qt_rev;
+  const int hq = g * group + hg;
+
+  const int q0 = qt * BM;
+  const int q_last = min(q0 + BM, a.Sq) - 1;
+  const int qw = q0 + wave * QW;
+  int qi[QB];
+  bool qv[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    qi[qb] = qw + 32 * qb + col;
+    qv[qb] = qi[qb] < a.Sq;
+  }
+
+  const __bf16* qbase = static_cast<const __bf16*>(a.q);
+  const __bf16* kbase = static_cast<const __bf16*>(a.k) + (int64_t)b * a.Sk * a.Hkv * D + (int64_t)g * D;
+  const __bf16* vbase = static_cast<const __bf16*>(a.v) + (int64_t)b * a.Sk * a.Hkv * D + (int64_t)g * D;
+  const int64_t q_rs = (int64_t)a.Hq * D;
+  const int64_t kv_rs = (int64_t)a.Hkv * D;
+
+  // Key tiles this workgroup visits.
+  int n_keys = a.Sk;
+  if (a.causal) {
+    const int64_t last_visible = a.q_offset + q_last - a.kv_offset;
+    n_keys = (int)max<int64_t>(0, min<int64_t>((int64_t)a.Sk, last_visible + 1));
+  }
+  int kt_begin = 0, kt_end = (n_keys + BN - 1) / BN;
+  const int32_t* seg_row = nullptr;
+  int seg_q[QB];
+  if constexpr (kSeg) {
+    seg_row = a.seg + (int64_t)b * a.seg_len;
+    const int lo = seg_row[a.q_offset + q0], hi = seg_row[a.q_offset + q_last];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) seg_q[qb] = qv[qb] ? seg_row[a.q_offset + qi[qb]] : lo;
+    const int32_t* seg_k = seg_row + a.kv_offset;
+    int first_live = kt_end, last_live = -1;
+    for (int base = 0; base < kt_end; base += 64) {
+      const int t = base + lane;
+      bool live = false;
+      if (t < kt_end) {
+        const int k_first = t * BN;
+        const int k_last = min((t + 1) * BN, a.Sk) - 1;
+        live = seg_k[k_last] >= lo && seg_k[k_first] <= hi;
+      }
+      const uint64_t mask = __ballot(live);
+      if (mask) {
+        first_live = min(first_live, base + (int)__builtin_ctzll(mask));
+        last_live = max(last_live, base + 63 - (int)__builtin_clzll(mask));
+      }
+    }
+    kt_begin = first_live;
+    kt_end = max(first_live, last_live + 1);
+  }
+
+  // Q operands (B of S^T = K Q^T).
+  bf16x8 qf[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const __bf16* qrow = qbase + ((int64_t)b * a.Sq + (qv[qb] ? qi[qb] : 0)) * q_rs + (int64_t)hq * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[qb][s] = qv[qb] ? load_bf16x8(qrow + 16 * s) : bf16x8{};
+  }
+
+  f32x16 oacc[QB][4];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[qb][db] = f32x16{};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.0f;
+  }
+  f32x16 s_next[QB];
+
+  // Register prefetch of one 32-row tile: 512 chunks of 16 bytes, 2 per thread;
+  // 16 consecutive lanes read one 256-byte row (coalesced) and write it to the
+  // row's swizzled chunk positions (conflict-free).
+  u32x4 kreg[2], vreg[2];
+  auto fetch = [&](const __bf16* base, int t, u32x4* reg) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int u = tid + r * kD128Threads;
+      const int row = u >> 4, c = u & 15;
+      const int key = min(t * BN + row, a.Sk - 1);
+      reg[r] = *reinterpret_cast<const u32x4*>(base + (int64_t)key * kv_rs + c * 8);
+    }
+  };
+  auto put = [&](__bf16* tile, const u32x4* reg) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int u = tid + r * kD128Threads;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(tile) + tile_off(u >> 4, u & 15)) = reg[r];
+    }
+  };
+  // S^T of one key tile; each K operand feeds QB MFMAs.
+  auto qk = [&](const __bf16* ktile) {
+    bf16x8 kf[8];
+    const int row = key_of_row(col);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = read_chunk(ktile, row, 2 * s + half);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s_next[qb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s_next[qb] = mfma_bf16(kf[s], qf[qb][s], s_next[qb]);
+  };
+
+  if (kt_begin < kt_end) {
+    fetch(kbase, kt_begin, kreg);
+    fetch(vbase, kt_begin, vreg);
+    put(kbuf[0], kreg);
+    put(vbuf[0], vreg);
+    if (kPipe && kt_begin + 1 < kt_end) {
+      fetch(kbase, kt_begin + 1, kreg);
+      put(kbuf[1], kreg);
+    }
+    __syncthreads();
+    if constexpr (kPipe) qk(kbuf[0]);
+  }
+  for (int t = kt_begin; t < kt_end; ++t) {
+    const int cur = (t - kt_begin) & 1;
+    __syncthreads();  // tiles of this step visible; every wave is done with step t-1 (or the prologue)
+    const bool more1 = t + 1 < kt_end, more2 = t + 2 < kt_end;
+    f32x16 sc[QB];
+    if constexpr (kPipe) {
+      if (more2) fetch(kbase, t + 2, kreg);
+      if (more1) fetch(vbase, t + 1, vreg);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc[qb] = s_next[qb];
+      if (more1) qk(kbuf[cur ^ 1]);
+    } else {
+      if (more1) {
+        fetch(kbase, t + 1, kreg);
+        fetch(vbase, t + 1, vreg);
+      }
+      qk(kbuf[cur]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc[qb] = s_next[qb];
+    }
+
+    const int k0 = t * BN;
+    bool partial = (k0 + BN > a.Sk);
+    if (a.causal) partial |= (a.kv_offset + k0 + BN - 1 > a.q_offset + qw);
+    if constexpr (kSeg) partial = true;
+    if (partial) {
+      // Per-element visibility: key index of register i in half h is k0 + 16h + i.
+      int segk[16];
+      if constexpr (kSeg) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kj = k0 + 16 * half + i;
+          segk[i] = kj < a.Sk ? seg_row[a.kv_offset + kj] : INT32_MIN;
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kj = k0 + 16 * half + i;
+          bool vis = kj < a.Sk;
+          if (a.causal) vis = vis && (a.kv_offset + kj <= a.q_offset + qi[qb]);
+          if constexpr (kSeg) vis = vis && (segk[i] == seg_q[qb]);
+          sc[qb][i] = vis ? sc[qb][i] : -INFINITY;
+        }
+    }
+
+    float tmax[QB];
+    bool grow[QB];
+    bool any_grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float r = sc[qb][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) r = fmaxf(r, sc[qb][i]);
+      r = fmaxf(r, __shfl_xor(r, 32));
+      tmax[qb] = r * a.scale_log2;
+      grow[qb] = tmax[qb] > m_run[qb] + kSlack;
+      any_grow |= grow[qb];
+    }
+    if (__ballot(any_grow)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float al = grow[qb] ? exp2_fast(m_run[qb] - tmax[qb]) : 1.0f;
+        if (grow[qb]) m_run[qb] = tmax[qb];
+        l_run[qb] *= al;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[qb][db] *= al;
+      }
+    }
+    bf16x8 pf[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float neg_m = (m_run[qb] == -INFINITY) ? 0.0f : -m_run[qb];
+      float p[16];
+      float psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = exp2_fast(__builtin_fmaf(sc[qb][i], a.scale_log2, neg_m));
+        psum += p[i];
+      }
+      l_run[qb] += psum;
+      pf[qb][0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      pf[qb][1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+    }
+    // O^T += V^T P^T: register 8m+j of half h holds key 16h + 8m + j.
+    const __bf16* vread = vbuf[cur];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x8 vf[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vf[db] = read_transposed(vread, 16 * half + 8 * m, 32 * db, lane);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma_bf16(vf[db], pf[qb][m], oacc[qb][db]);
+    }
+    if constexpr (kPipe) {
+      // K(t+2) replaces K(t) (read during step t-1); V(t+1) replaces V(t-1).
+      if (more2) put(kbuf[cur], kreg);
+      if (more1) put(vbuf[cur ^ 1], vreg);
+    } else {
+      // Other waves may still read this step's tiles: the next step's barrier
+      // orders these stores after them (the tiles go to the other slot).
+      if (more1) {
+        put(kbuf[cur ^ 1], kreg);
+        put(vbuf[cur ^ 1], vreg);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const bool live = l_tot > 0.0f;
+    const float inv = live ? 1.0f / l_tot : 0.0f;
+    if (qv[qb]) {
+      float* orow = a.o + ((int64_t)b * a.Sq + qi[qb]) * q_rs + (int64_t)hq * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 v = {oacc[qb][db][4 * r4] * inv, oacc[qb][db][4 * r4 + 1] * inv, oacc[qb][db][4 * r4 + 2] * inv,
+                     oacc[qb][db][4 * r4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * half) = v;
+        }
+      if (half == 0)
+        a.lse[((int64_t)b * a.Hq + hq) * a.Sq + qi[qb]] = live ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
 template <typename T, int D>
 ra_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
   const int64_t n_wg = (int64_t)args.B * args.Hq * args.n_qtiles;
   if (n_wg > INT32_MAX) return fail(RA_ERR_INVALID_ARGUMENT, "too many workgroups");
+  if constexpr (std::is_same<T, __bf16>::value && D == 128) {
+    FwdArgs a2 = args;
+    a2.n_qtiles = (args.Sq + kD128BM - 1) / kD128BM;
+    const int64_t n2 = (int64_t)args.B * args.Hq * a2.n_qtiles;
+    if (args.seg != nullptr)
+      hipLaunchKernelGGL((fwd_step_d128_kernel<true>), dim3((unsigned)n2), dim3(kD128Threads), 0, stream, a2);
+    else
+      hipLaunchKernelGGL((fwd_step_d128_kernel<false>), dim3((unsigned)n2), dim3(kD128Threads), 0, stream, a2);
+    return check_launch("ring_attn_fwd_step");
+  }
   if (args.seg != nullptr)
     hipLaunchKernelGGL((fwd_step_kernel<T, D, true>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, args);
   else

@@ -101,6 +101,68 @@ struct Mfma<float> {
 // that accumulator register i of half-wave h holds key 16h + i.
 __device__ __forceinline__ int key_of_row(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
 
+// ---- LDS tiles of 128-element bf16 rows (256 B per row, no padding) ------------------
+// The 16 chunks of 16 bytes of row r are stored XOR-swizzled at chunk position
+// c ^ swz(r).  swz uses bits 0,1,2 and 4 of the row, which makes both operand read
+// patterns of the kernels conflict-free: 16 lanes reading one logical chunk of rows
+// {0-3, 16-19, 4-7, 20-23} (or the +8 set), and 16 lanes transposing 4 consecutive
+// rows x 32 bytes.  Rows are filled by direct global->LDS loads (lane l of a wave
+// writes bytes [16l, 16l+16) of a 1 KiB block = 4 rows), so the swizzle is applied
+// on the global side by choosing which chunk each lane fetches.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 4) & 1); }
+
+__device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
+
+// Wait until every global->LDS load issued by this wave has landed.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Copies `rows` rows of 128 bf16 (row r from src + r*row_stride, clamped to
+// valid_rows-1 so every fetch stays in bounds) into a swizzled LDS tile.  The
+// tile's 1 KiB blocks are spread over the workgroup's `waves` waves.
+template <int ROWS, int WAVES>
+__device__ __forceinline__ void load_rows_lds(__bf16* tile, const __bf16* src, int64_t row_stride, int valid_rows,
+                                              int wave, int lane) {
+  static_assert(ROWS % (4 * WAVES) == 0, "rows per wave must be a multiple of 4");
+  constexpr int kBlocks = ROWS / 4 / WAVES;
+#pragma unroll
+  for (int r = 0; r < kBlocks; ++r) {
+    const int blk = wave * kBlocks + r;
+    const int row = blk * 4 + (lane >> 4);
+    const int chunk = (lane & 15) ^ swz(row);
+    const int grow = min(row, valid_rows - 1);
+    const __bf16* g = src + (int64_t)grow * row_stride + chunk * 8;
+    __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)(reinterpret_cast<char*>(tile) + blk * 1024), 16, 0, 0);
+  }
+}
+
+// 16-byte operand read: logical chunk `chunk` of row `row` of a swizzled tile.
+__device__ __forceinline__ bf16x8 read_chunk(const __bf16* tile, int row, int chunk) {
+  return load_bf16x8(reinterpret_cast<const char*>(tile) + tile_off(row, chunk));
+}
+
+// Transposing operand read (ds_read_b64_tr_b16) of a swizzled tile: lane l gets, as
+// 8 bf16, column col0 + (l % 32) of rows row8 .. row8+7 (row8 may differ between the
+// two half-waves).  Each call issues two transposing reads of 4 rows.  Within a
+// 16-lane group, source lane s = m + 4k addresses row (base + k) at columns
+// colbase + 4m .. +3; the hardware returns to lane j element (j % 4) of the
+// addresses of lanes j/4 + 4k, k = 0..3, i.e. rows base+0..3 of column colbase + j.
+__device__ __forceinline__ bf16x8 read_transposed(const __bf16* tile, int row8, int col0, int lane) {
+  const int s = lane & 15;
+  const int m = s & 3, k = s >> 2;
+  const int colbase = col0 + (lane & 16);           // 16-column half of the 32 columns
+  const int c = (colbase >> 3) + (m >> 1);          // logical 16-byte chunk
+  const int sub8 = (m & 1) * 8;                     // byte offset inside the chunk
+  typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+  const char* base = reinterpret_cast<const char*>(tile);
+  const int r0 = row8 + k, r1 = row8 + 4 + k;
+  v4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4*)(base + tile_off(r0, c) + sub8));
+  v4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4*)(base + tile_off(r1, c) + sub8));
+  bf16x8 out = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  return out;
+}
+
 // Workgroup -> XCD remap.  Consecutive workgroup ids are dispatched round-robin
 // over the 8 XCDs of an MI355X; this returns a logical id such that each XCD
 // receives one contiguous range of logical ids (so workgroups that share K/V
