@@ -1,0 +1,64 @@
+// Shared declarations of the backward ring-step kernels.
+#pragma once
+
+#include "ra_device.h"
+#include "ra_host.h"
+
+#ifndef RA_DKDV_QBLOCKS
+#define RA_DKDV_QBLOCKS 2  // 32-query blocks per staged query tile of the bf16 d=128 dK/dV kernel
+#endif
+#ifndef RA_DKDV_WAVES
+#define RA_DKDV_WAVES 4  // waves (x 32 keys) per dK/dV workgroup of the bf16 d=128 path
+#endif
+
+namespace ra {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* d_o;
+  const float* lse;
+  const float* delta;
+  const int32_t* seg;
+  int64_t seg_len;
+  float* dq;
+  float* dk;
+  float* dv;
+  int B, Sq, Sk, Hq, Hkv;
+  int64_t q_offset, kv_offset;
+  int causal;
+  float scale;
+  float scale_log2;
+  int n_tiles;  // key tiles per (b, kv head) for dkdv; query tiles per (b, q head) for dq
+};
+
+// Contiguous range [begin, end) of tiles (of `tile` items over `n` items of the
+// row starting at `row`) whose segment-id range meets [lo, hi].  Segment ids are
+// nondecreasing along the row, so the live tiles are contiguous.  Wave-uniform.
+__device__ __forceinline__ void seg_tile_range(const int32_t* row, int n, int tile, int t_begin, int t_end,
+                                               int lo, int hi, int& out_begin, int& out_end) {
+  const int lane = threadIdx.x & 63;
+  int first = t_end, last = -1;
+  for (int base = t_begin; base < t_end; base += 64) {
+    const int t = base + lane;
+    bool live = false;
+    if (t < t_end) {
+      const int a = t * tile;
+      const int z = min((t + 1) * tile, n) - 1;
+      live = row[z] >= lo && row[a] <= hi;
+    }
+    const uint64_t mask = __ballot(live);
+    if (mask) {
+      first = min(first, base + (int)__builtin_ctzll(mask));
+      last = max(last, base + 63 - (int)__builtin_clzll(mask));
+    }
+  }
+  out_begin = first;
+  out_end = last + 1;
+}
+
+// bf16, head_dim 128 (bwd_d128.hip): dK/dV kernel then dQ kernel on `stream`.
+ra_status launch_bwd_d128(BwdArgs args, hipStream_t stream);
+
+}  // namespace ra

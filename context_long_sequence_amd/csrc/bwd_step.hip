@@ -20,59 +20,15 @@
 //    and walks the key tiles like the forward (query in the lane); K is staged
 //    row-major and transposed, V row-major.
 // dK/dV and dQ are read-modify-written (+=) by exactly one workgroup each.
-#include "ra_device.h"
-#include "ra_host.h"
+#include <type_traits>
+
+#include "bwd_d128.h"
 
 namespace ra {
 namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-
-struct BwdArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* d_o;
-  const float* lse;
-  const float* delta;
-  const int32_t* seg;
-  int64_t seg_len;
-  float* dq;
-  float* dk;
-  float* dv;
-  int B, Sq, Sk, Hq, Hkv;
-  int64_t q_offset, kv_offset;
-  int causal;
-  float scale;
-  float scale_log2;
-  int n_tiles;  // key tiles per (b, kv head) for dkdv; query tiles per (b, q head) for dq
-};
-
-// Contiguous range [begin, end) of tiles (of `tile` items over `n` items of the
-// row starting at `row`) whose segment-id range meets [lo, hi].  Segment ids are
-// nondecreasing along the row, so the live tiles are contiguous.  Wave-uniform.
-__device__ __forceinline__ void seg_tile_range(const int32_t* row, int n, int tile, int t_begin, int t_end,
-                                               int lo, int hi, int& out_begin, int& out_end) {
-  const int lane = threadIdx.x & 63;
-  int first = t_end, last = -1;
-  for (int base = t_begin; base < t_end; base += 64) {
-    const int t = base + lane;
-    bool live = false;
-    if (t < t_end) {
-      const int a = t * tile;
-      const int z = min((t + 1) * tile, n) - 1;
-      live = row[z] >= lo && row[a] <= hi;
-    }
-    const uint64_t mask = __ballot(live);
-    if (mask) {
-      first = min(first, base + (int)__builtin_ctzll(mask));
-      last = max(last, base + 63 - (int)__builtin_clzll(mask));
-    }
-  }
-  out_begin = first;
-  out_end = last + 1;
-}
 
 // Stores a pair of 16-byte rows (items 2p and 2p+1, columns ch*E .. ch*E+E-1) into a
 // transposed LDS tile: dst[(ch*E + j) * pitch + 2p + {0,1}].
@@ -553,6 +509,9 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
 
 template <typename T, int D>
 ra_status launch_bwd(BwdArgs args, hipStream_t stream) {
+#ifndef RA_BWD_GENERIC_ONLY
+  if constexpr (std::is_same<T, __bf16>::value && D == 128) return launch_bwd_d128(args, stream);
+#endif
   // dK/dV: one workgroup per (b, kv head, 128-key tile).
   args.n_tiles = (args.Sk + 32 * kWaves - 1) / (32 * kWaves);
   int64_t n_wg = (int64_t)args.B * args.Hkv * args.n_tiles;
