@@ -1,0 +1,201 @@
+// dQ of one backward ring step for the hot shape (bf16, head_dim 128):
+//   dQ_i += scale * sum_j P_ij (dP_ij - delta_i) k_j,  P recomputed from the final
+// log-sum-exp (archcrux, "sequence-parallel long-context attention OOM").
+// 4 waves x 32 queries of one query head walk the key tiles of the chunk; K and
+// V tiles are register-prefetched into double-buffered, swizzled, row-major LDS
+// tiles, and the K^T operands of dQ^T += K^T dS^T come from transposing reads of
+// the same K tile.
+#include "bwd_d128.h"
+
+#ifndef RA_DQ_BATCH
+#define RA_DQ_BATCH 0  // 1: issue each MFMA chain's operand reads before its first MFMA (costs the second wave per SIMD)
+#endif
+
+namespace ra {
+namespace {
+
+constexpr int kD = kD128;
+constexpr int kTile = kD128Tile;
+
+// ------------------------------------------------------------------------------------
+// dQ: 4 waves x 32 queries of one query head; walks the key tiles of the chunk.
+// ------------------------------------------------------------------------------------
+constexpr int kDqWaves = 4;
+constexpr int kDqThreads = 64 * kDqWaves;
+
+template <bool kSeg>
+__global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) __bf16 kbuf[2][kTile * kD];
+  __shared__ __attribute__((aligned(1024))) __bf16 vbuf[2][kTile * kD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int group = a.Hq / a.Hkv;
+  int rem = logical;
+  const int qt_rev = rem % a.n_tiles;
+  rem /= a.n_tiles;
+  const int hg = rem % group;
+  rem /= group;
+  const int g = rem % a.Hkv;
+  const int b = rem / a.Hkv;
+  const int qt = a.n_tiles - 1 - qt_rev;
+  const int hq = g * group + hg;
+
+  constexpr int BM = 32 * kDqWaves;
+  const int q0 = qt * BM;
+  const int q_last = min(q0 + BM, a.Sq) - 1;
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + col;
+  const bool q_valid = qi < a.Sq;
+  const int64_t qg = a.q_offset + qi;
+
+  const int64_t q_rs = (int64_t)a.Hq * kD, kv_rs = (int64_t)a.Hkv * kD;
+  const __bf16* kbase = static_cast<const __bf16*>(a.k) + (int64_t)b * a.Sk * kv_rs + (int64_t)g * kD;
+  const __bf16* vbase = static_cast<const __bf16*>(a.v) + (int64_t)b * a.Sk * kv_rs + (int64_t)g * kD;
+
+  int n_keys = a.Sk;
+  if (a.causal) {
+    const int64_t last_visible = a.q_offset + q_last - a.kv_offset;
+    n_keys = (int)max<int64_t>(0, min<int64_t>((int64_t)a.Sk, last_visible + 1));
+  }
+  int kt_begin = 0, kt_end = (n_keys + kTile - 1) / kTile;
+  int seg_q = 0;
+  const int32_t* seg_row = nullptr;
+  if constexpr (kSeg) {
+    seg_row = a.seg + (int64_t)b * a.seg_len;
+    const int lo = seg_row[a.q_offset + q0], hi = seg_row[a.q_offset + q_last];
+    seg_q = q_valid ? seg_row[a.q_offset + qi] : lo;
+    int sb, se;
+    seg_tile_range(seg_row + a.kv_offset, a.Sk, kTile, 0, kt_end, lo, hi, sb, se);
+    kt_begin = sb;
+    kt_end = max(sb, se);
+  }
+
+  bf16x8 qf[8], dof[8];
+  {
+    const int64_t off = ((int64_t)b * a.Sq + (q_valid ? qi : 0)) * q_rs + (int64_t)hq * kD + 8 * half;
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + off;
+    const __bf16* dp = static_cast<const __bf16*>(a.d_o) + off;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qf[s] = q_valid ? load_bf16x8(qp + 16 * s) : bf16x8{};
+      dof[s] = q_valid ? load_bf16x8(dp + 16 * s) : bf16x8{};
+    }
+  }
+  const int64_t li = ((int64_t)b * a.Hq + hq) * a.Sq + (q_valid ? qi : 0);
+  const float lse_q = q_valid ? a.lse[li] : -INFINITY;
+  const float neg_lse2 = lse_q == -INFINITY ? -INFINITY : -lse_q * kLog2e;
+  const float dl = q_valid ? a.delta[li] : 0.0f;
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
+
+  TileStage<kDqThreads> ks, vs;
+  if (kt_begin < kt_end) {
+    ks.fetch(kbase, kv_rs, kt_begin * kTile, a.Sk, tid);
+    vs.fetch(vbase, kv_rs, kt_begin * kTile, a.Sk, tid);
+    ks.put(kbuf[0], tid);
+    vs.put(vbuf[0], tid);
+  }
+  for (int t = kt_begin; t < kt_end; ++t) {
+    const int cur = (t - kt_begin) & 1;
+    __syncthreads();  // tile t visible; every wave is done with tile t-1
+    const bool more = t + 1 < kt_end;
+    if (more) {
+      ks.fetch(kbase, kv_rs, (t + 1) * kTile, a.Sk, tid);
+      vs.fetch(vbase, kv_rs, (t + 1) * kTile, a.Sk, tid);
+    }
+    const __bf16* kt_ = kbuf[cur];
+    const __bf16* vt_ = vbuf[cur];
+    const int k0 = t * kTile;
+    bool partial = (k0 + kTile > a.Sk) || (qw + 32 > a.Sq);  // wave-uniform
+    if (a.causal) partial |= (a.kv_offset + k0 + kTile - 1 > a.q_offset + qw);
+    if constexpr (kSeg) partial = true;
+
+    // S^T = K Q^T and dP^T = V dO^T; register i of half h = key k0 + 16h + i.
+    f32x16 st = f32x16{}, dpt = f32x16{};
+    {
+      // Issue all 16 operand reads before the first MFMA, then interleave the two
+      // independent chains (keeps the LDS latency off the MFMA issue path).
+      const int row = key_of_row(col);
+      bf16x8 fk[8], fv[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) fk[s] = read_chunk(kt_, row, 2 * s + half);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) fv[s] = read_chunk(vt_, row, 2 * s + half);
+      if constexpr (RA_DQ_BATCH) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        st = mfma_bf16(fk[s], qf[s], st);
+        dpt = mfma_bf16(fv[s], dof[s], dpt);
+      }
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(st[i], a.scale_log2, neg_lse2));
+    if (partial) {  // one wave-uniform branch around the element mask
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kj = k0 + 16 * half + i;
+        bool vis = q_valid && kj < a.Sk;
+        if (a.causal) vis = vis && (a.kv_offset + kj <= qg);
+        if constexpr (kSeg) vis = vis && (kj < a.Sk ? seg_row[a.kv_offset + kj] == seg_q : false);
+        p[i] = vis ? p[i] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dpt[i] - dl);
+    // dQ^T += K^T dS^T: K^T rows (keys 16h + 8m + j) by transposing reads of the K tile.
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 sf = to_bf16x8(ds[8 * m], ds[8 * m + 1], ds[8 * m + 2], ds[8 * m + 3], ds[8 * m + 4],
+                                  ds[8 * m + 5], ds[8 * m + 6], ds[8 * m + 7]);
+      bf16x8 kt[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) kt[db] = read_transposed(kt_, 16 * half + 8 * m, 32 * db, lane);
+      if constexpr (RA_DQ_BATCH) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) dq[db] = mfma_bf16(kt[db], sf, dq[db]);
+    }
+    if (more) {
+      ks.put(kbuf[cur ^ 1], tid);  // slot of tile t-1, released by this step's barrier
+      vs.put(vbuf[cur ^ 1], tid);
+    }
+  }
+
+  if (q_valid) {
+    float* row = a.dq + ((int64_t)b * a.Sq + qi) * q_rs + (int64_t)hq * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4* p = reinterpret_cast<f32x4*>(row + 32 * db + 8 * r4 + 4 * half);
+        f32x4 cur = *p;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cur[j] += a.scale * dq[db][4 * r4 + j];
+        *p = cur;
+      }
+  }
+}
+
+}  // namespace
+
+ra_status launch_dq_d128(BwdArgs args, hipStream_t stream) {
+  args.n_tiles = (args.Sq + 32 * kDqWaves - 1) / (32 * kDqWaves);
+  const int64_t n_wg = (int64_t)args.B * args.Hq * args.n_tiles;
+  if (n_wg > INT32_MAX) return fail(RA_ERR_INVALID_ARGUMENT, "too many workgroups");
+  if (args.seg)
+    hipLaunchKernelGGL((dq_d128_kernel<true>), dim3((unsigned)n_wg), dim3(kDqThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((dq_d128_kernel<false>), dim3((unsigned)n_wg), dim3(kDqThreads), 0, stream, args);
+  return check_launch("ring_attn_bwd_step (dQ)");
+}
+
+ra_status launch_bwd_d128(BwdArgs args, hipStream_t stream) {
+  const ra_status st = launch_dkdv_d128(args, stream);
+  if (st != RA_OK) return st;
+  return launch_dq_d128(args, stream);
+}
+
+}  // namespace ra

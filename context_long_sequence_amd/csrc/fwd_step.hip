@@ -25,6 +25,10 @@
 #include <type_traits>
 
 #include "ra_device.h"
+
+#ifndef RA_FWD_BATCH
+#define RA_FWD_BATCH 1  // issue each MFMA chain's operand reads before its first MFMA
+#endif
 #include "ra_host.h"
 
 namespace ra {
@@ -497,6 +501,7 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
     const int row = key_of_row(col);
 #pragma unroll
     for (int s = 0; s < 8; ++s) kf[s] = read_chunk(ktile, row, 2 * s + half);
+    if constexpr (RA_FWD_BATCH) __builtin_amdgcn_sched_barrier(0);  // all K reads in flight before the first MFMA
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s_next[qb] = f32x16{};
 #pragma unroll
@@ -609,6 +614,7 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
       bf16x8 vf[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) vf[db] = read_transposed(vread, 16 * half + 8 * m, 32 * db, lane);
+      if constexpr (RA_FWD_BATCH) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
