@@ -77,10 +77,13 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     qt_begin = (int)min<int64_t>((int64_t)n_qt, max<int64_t>(0, first_q) / QT);
   }
   int seg_k = 0;
+  int seg_w_lo = 0, seg_w_hi = 0;  // segment ids of the wave's first and last key
   const int32_t* seg_row = nullptr;
   if constexpr (kSeg) {
     seg_row = a.seg + (int64_t)b * a.seg_len;
     seg_k = k_valid ? seg_row[kgl] : INT32_MIN;
+    seg_w_lo = seg_row[a.kv_offset + min(kw, a.Sk - 1)];
+    seg_w_hi = seg_row[a.kv_offset + min(kw + 32, a.Sk) - 1];
     const int lo = seg_row[a.kv_offset + k0], hi = seg_row[a.kv_offset + k_last];
     int sb, se;
     seg_tile_range(seg_row + a.q_offset, a.Sq, QT, qt_begin, qt_end, lo, hi, sb, se);
@@ -128,7 +131,13 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
       const int q0 = qtile0 + 32 * qb;
       bool partial = (q0 + 32 > a.Sq) || (kw + 32 > a.Sk);  // wave-uniform
       if (a.causal) partial |= (a.kv_offset + kw + 31 > a.q_offset + q0);
-      if constexpr (kSeg) partial = true;
+      if constexpr (kSeg) {
+        // Segment ids are nondecreasing: only blocks that straddle a segment
+        // boundary need the per-element segment test.
+        const int sq_lo = __builtin_bit_cast(int, xs[2 * QT + 32 * qb]);
+        const int sq_hi = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 31]);
+        partial |= !(sq_lo == sq_hi && sq_lo == seg_w_lo && seg_w_lo == seg_w_hi);
+      }
       if (a.causal && a.kv_offset + kw > a.q_offset + q0 + 31) continue;  // block entirely before these keys
 
       // S = Q K^T and dP = dO V^T: lane = key, register i of half h = query q0 + 16h + i.

@@ -2,9 +2,9 @@
 //   dQ_i += scale * sum_j P_ij (dP_ij - delta_i) k_j,  P recomputed from the final
 // log-sum-exp (archcrux, "sequence-parallel long-context attention OOM").
 // 4 waves x 32 queries of one query head walk the key tiles of the chunk; K and
-// V tiles are register-prefetched into double-buffered, swizzled, row-major LDS
-// tiles, and the K^T operands of dQ^T += K^T dS^T come from transposing reads of
-// the same K tile.
+// V tiles are copied global -> LDS (swizzled, row-major) two steps ahead into a
+// ring of three slots, and the K^T operands of dQ^T += K^T dS^T come from
+// transposing reads of the same K tile.
 #include "bwd_d128.h"
 
 #ifndef RA_DQ_BATCH
@@ -25,8 +25,13 @@ constexpr int kDqThreads = 64 * kDqWaves;
 
 template <bool kSeg>
 __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) __bf16 kbuf[2][kTile * kD];
-  __shared__ __attribute__((aligned(1024))) __bf16 vbuf[2][kTile * kD];
+  // Three K and three V tile slots, each its own array (see the copy loop below).
+  __shared__ __attribute__((aligned(1024))) __bf16 ks0[kTile * kD];
+  __shared__ __attribute__((aligned(1024))) __bf16 ks1[kTile * kD];
+  __shared__ __attribute__((aligned(1024))) __bf16 ks2[kTile * kD];
+  __shared__ __attribute__((aligned(1024))) __bf16 vs0[kTile * kD];
+  __shared__ __attribute__((aligned(1024))) __bf16 vs1[kTile * kD];
+  __shared__ __attribute__((aligned(1024))) __bf16 vs2[kTile * kD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -60,11 +65,14 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
   }
   int kt_begin = 0, kt_end = (n_keys + kTile - 1) / kTile;
   int seg_q = 0;
+  int seg_w_lo = 0, seg_w_hi = 0;  // segment ids of the wave's first and last query
   const int32_t* seg_row = nullptr;
   if constexpr (kSeg) {
     seg_row = a.seg + (int64_t)b * a.seg_len;
     const int lo = seg_row[a.q_offset + q0], hi = seg_row[a.q_offset + q_last];
     seg_q = q_valid ? seg_row[a.q_offset + qi] : lo;
+    seg_w_lo = seg_row[a.q_offset + min(qw, a.Sq - 1)];
+    seg_w_hi = seg_row[a.q_offset + min(qw + 32, a.Sq) - 1];
     int sb, se;
     seg_tile_range(seg_row + a.kv_offset, a.Sk, kTile, 0, kt_end, lo, hi, sb, se);
     kt_begin = sb;
@@ -91,77 +99,95 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
 
-  TileStage<kDqThreads> ks, vs;
-  if (kt_begin < kt_end) {
-    ks.fetch(kbase, kv_rs, kt_begin * kTile, a.Sk, tid);
-    vs.fetch(vbase, kv_rs, kt_begin * kTile, a.Sk, tid);
-    ks.put(kbuf[0], tid);
-    vs.put(vbuf[0], tid);
-  }
-  for (int t = kt_begin; t < kt_end; ++t) {
-    const int cur = (t - kt_begin) & 1;
-    __syncthreads();  // tile t visible; every wave is done with tile t-1
-    const bool more = t + 1 < kt_end;
-    if (more) {
-      ks.fetch(kbase, kv_rs, (t + 1) * kTile, a.Sk, tid);
-      vs.fetch(vbase, kv_rs, (t + 1) * kTile, a.Sk, tid);
-    }
-    const __bf16* kt_ = kbuf[cur];
-    const __bf16* vt_ = vbuf[cur];
-    const int k0 = t * kTile;
-    bool partial = (k0 + kTile > a.Sk) || (qw + 32 > a.Sq);  // wave-uniform
-    if (a.causal) partial |= (a.kv_offset + k0 + kTile - 1 > a.q_offset + qw);
-    if constexpr (kSeg) partial = true;
+  // Copies key tile t (K and V, 32 rows each) global -> LDS without registers:
+  // two 16-byte copies per wave and tensor.
+  auto issue = [&](int t, __bf16* kdst, __bf16* vdst) {
+    load_rows_lds<kTile, kDqWaves>(kdst, kbase + (int64_t)t * kTile * kv_rs, kv_rs, a.Sk - t * kTile, wave, lane);
+    load_rows_lds<kTile, kDqWaves>(vdst, vbase + (int64_t)t * kTile * kv_rs, kv_rs, a.Sk - t * kTile, wave, lane);
+  };
+  constexpr int kCopiesPerTile = 2 * (kTile / 4 / kDqWaves);
 
-    // S^T = K Q^T and dP^T = V dO^T; register i of half h = key k0 + 16h + i.
-    f32x16 st = f32x16{}, dpt = f32x16{};
-    {
-      // Issue all 16 operand reads before the first MFMA, then interleave the two
-      // independent chains (keeps the LDS latency off the MFMA issue path).
-      const int row = key_of_row(col);
-      bf16x8 fk[8], fv[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) fk[s] = read_chunk(kt_, row, 2 * s + half);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) fv[s] = read_chunk(vt_, row, 2 * s + half);
-      if constexpr (RA_DQ_BATCH) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        st = mfma_bf16(fk[s], qf[s], st);
-        dpt = mfma_bf16(fv[s], dof[s], dpt);
+  auto compute = [&](int t, const __bf16* kt_, const __bf16* vt_) {
+      const int k0 = t * kTile;
+      bool partial = (k0 + kTile > a.Sk) || (qw + 32 > a.Sq);  // wave-uniform
+      if (a.causal) partial |= (a.kv_offset + k0 + kTile - 1 > a.q_offset + qw);
+      if constexpr (kSeg) {
+        // Segment ids are nondecreasing: only blocks that straddle a segment
+        // boundary need the per-element segment test.
+        const int sk_lo = seg_row[a.kv_offset + k0];
+        const int sk_hi = seg_row[a.kv_offset + min(k0 + kTile, a.Sk) - 1];
+        partial |= !(sk_lo == sk_hi && sk_lo == seg_w_lo && seg_w_lo == seg_w_hi);
       }
-    }
-    float p[16], ds[16];
+
+      // S^T = K Q^T and dP^T = V dO^T; register i of half h = key k0 + 16h + i.
+      f32x16 st = f32x16{}, dpt = f32x16{};
+      {
+        // Issue all 16 operand reads before the first MFMA, then interleave the two
+        // independent chains (keeps the LDS latency off the MFMA issue path).
+        const int row = key_of_row(col);
+        bf16x8 fk[8], fv[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(st[i], a.scale_log2, neg_lse2));
-    if (partial) {  // one wave-uniform branch around the element mask
+        for (int s = 0; s < 8; ++s) fk[s] = read_chunk(kt_, row, 2 * s + half);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kj = k0 + 16 * half + i;
-        bool vis = q_valid && kj < a.Sk;
-        if (a.causal) vis = vis && (a.kv_offset + kj <= qg);
-        if constexpr (kSeg) vis = vis && (kj < a.Sk ? seg_row[a.kv_offset + kj] == seg_q : false);
-        p[i] = vis ? p[i] : 0.0f;
+        for (int s = 0; s < 8; ++s) fv[s] = read_chunk(vt_, row, 2 * s + half);
+        if constexpr (RA_DQ_BATCH) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          st = mfma_bf16(fk[s], qf[s], st);
+          dpt = mfma_bf16(fv[s], dof[s], dpt);
+        }
       }
-    }
+      float p[16], ds[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dpt[i] - dl);
-    // dQ^T += K^T dS^T: K^T rows (keys 16h + 8m + j) by transposing reads of the K tile.
+      for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(st[i], a.scale_log2, neg_lse2));
+      if (partial) {  // one wave-uniform branch around the element mask
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const bf16x8 sf = to_bf16x8(ds[8 * m], ds[8 * m + 1], ds[8 * m + 2], ds[8 * m + 3], ds[8 * m + 4],
-                                  ds[8 * m + 5], ds[8 * m + 6], ds[8 * m + 7]);
-      bf16x8 kt[4];
+        for (int i = 0; i < 16; ++i) {
+          const int kj = k0 + 16 * half + i;
+          bool vis = q_valid && kj < a.Sk;
+          if (a.causal) vis = vis && (a.kv_offset + kj <= qg);
+          if constexpr (kSeg) vis = vis && (kj < a.Sk ? seg_row[a.kv_offset + kj] == seg_q : false);
+          p[i] = vis ? p[i] : 0.0f;
+        }
+      }
 #pragma unroll
-      for (int db = 0; db < 4; ++db) kt[db] = read_transposed(kt_, 16 * half + 8 * m, 32 * db, lane);
-      if constexpr (RA_DQ_BATCH) __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dpt[i] - dl);
+      // dQ^T += K^T dS^T: K^T rows (keys 16h + 8m + j) by transposing reads of the K tile.
 #pragma unroll
-      for (int db = 0; db < 4; ++db) dq[db] = mfma_bf16(kt[db], sf, dq[db]);
-    }
-    if (more) {
-      ks.put(kbuf[cur ^ 1], tid);  // slot of tile t-1, released by this step's barrier
-      vs.put(vbuf[cur ^ 1], tid);
-    }
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 sf = to_bf16x8(ds[8 * m], ds[8 * m + 1], ds[8 * m + 2], ds[8 * m + 3], ds[8 * m + 4],
+                                    ds[8 * m + 5], ds[8 * m + 6], ds[8 * m + 7]);
+        bf16x8 kt[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) kt[db] = read_transposed(kt_, 16 * half + 8 * m, 32 * db, lane);
+        if constexpr (RA_DQ_BATCH) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dq[db] = mfma_bf16(kt[db], sf, dq[db]);
+      }
+  };
+
+  // One step: wait for tile t (copies issued two steps ago), publish it, start
+  // copying tile t+2 into the slot of tile t-1, compute.  Bare s_barrier (a
+  // workgroup fence would also drain the copies in flight); the empty asm
+  // statements keep the compiler from moving LDS accesses across it.
+  auto step = [&](int t, const __bf16* kc, const __bf16* vc, __bf16* kn, __bf16* vn) {
+    if (t + 1 < kt_end)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesPerTile);  // vmcnt(4): tile t+1 may stay in flight
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 2 < kt_end) issue(t + 2, kn, vn);
+    compute(t, kc, vc);
+  };
+
+  if (kt_begin < kt_end) issue(kt_begin, ks0, vs0);
+  if (kt_begin + 1 < kt_end) issue(kt_begin + 1, ks1, vs1);
+  for (int t = kt_begin; t < kt_end; t += 3) {
+    step(t, ks0, vs0, ks2, vs2);
+    if (t + 1 < kt_end) step(t + 1, ks1, vs1, ks0, vs0);
+    if (t + 2 < kt_end) step(t + 2, ks2, vs2, ks1, vs1);
   }
 
   if (q_valid) {

@@ -428,11 +428,14 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
   int kt_begin = 0, kt_end = (n_keys + BN - 1) / BN;
   const int32_t* seg_row = nullptr;
   int seg_q[QB];
+  int seg_w_lo = 0, seg_w_hi = 0;  // segment ids of the wave's first and last query
   if constexpr (kSeg) {
     seg_row = a.seg + (int64_t)b * a.seg_len;
     const int lo = seg_row[a.q_offset + q0], hi = seg_row[a.q_offset + q_last];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) seg_q[qb] = qv[qb] ? seg_row[a.q_offset + qi[qb]] : lo;
+    seg_w_lo = seg_row[a.q_offset + min(qw, a.Sq - 1)];
+    seg_w_hi = seg_row[a.q_offset + min(qw + QW, a.Sq) - 1];
     const int32_t* seg_k = seg_row + a.kv_offset;
     int first_live = kt_end, last_live = -1;
     for (int base = 0; base < kt_end; base += 64) {
@@ -546,7 +549,13 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
     const int k0 = t * BN;
     bool partial = (k0 + BN > a.Sk);
     if (a.causal) partial |= (a.kv_offset + k0 + BN - 1 > a.q_offset + qw);
-    if constexpr (kSeg) partial = true;
+    if constexpr (kSeg) {
+      // Segment ids are nondecreasing: the block needs the segment test only if the
+      // wave's queries and the tile's keys are not all in one and the same segment.
+      const int sk_lo = seg_row[a.kv_offset + k0];
+      const int sk_hi = seg_row[a.kv_offset + min(k0 + BN, a.Sk) - 1];
+      partial |= !(sk_lo == sk_hi && sk_lo == seg_w_lo && seg_w_lo == seg_w_hi);
+    }
     if (partial) {
       // Per-element visibility: key index of register i in half h is k0 + 16h + i.
       int segk[16];
