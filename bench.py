@@ -32,6 +32,37 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ring_bwd_step_64k_cp8_r7_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and headers of the library (name + contents)."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "context_long_sequence_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
+    the summary is missing or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.strip().split("=", 1) for line in f if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    v = kv.get(f"{kernel}.hbm_bytes_per_launch")
+    return float(v) if v else None
+
+
 def live_pairs_causal(C: int, rank: int) -> int:
     """Causal pairs of rank `rank` with contiguous chunks of C: rank*C^2 + C(C+1)/2."""
     return rank * C * C + C * (C + 1) // 2
@@ -182,15 +213,17 @@ def main():
         dom = max(("fwd_step", "bwd_step"), key=lambda n: per_step_ms.get(n, 0.0))
         if dom == "bwd_step" and t_bwd_step:
             achieved = f_bwd / CP / (t_bwd_step * 1e-3) / 1e12
-            roofline = {"kernel": "ring_attn_bwd_step (dkdv_kernel + dq_kernel)", "bound": "mfma",
+            roofline = {"kernel": "ring_attn_bwd_step (dK/dV kernel + dQ kernel)", "bound": "mfma",
                         "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                        "traffic": measured_traffic("ring_attn_bwd_step"),
                         "avg_launch_ms": round(t_bwd_step, 4), "flop_per_launch": f_bwd / CP}
         elif t_fwd_step:
             achieved = f_fwd / CP / (t_fwd_step * 1e-3) / 1e12
-            roofline = {"kernel": "ring_attn_fwd_step (fwd_step_kernel)", "bound": "mfma",
+            roofline = {"kernel": "ring_attn_fwd_step", "bound": "mfma",
                         "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                        "traffic": measured_traffic("ring_attn_fwd_step"),
                         "avg_launch_ms": round(t_fwd_step, 4), "flop_per_launch": f_fwd / CP}
 
     extra = {
