@@ -361,33 +361,30 @@ __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a) {
 
 
 // ------------------------------------------------------------------------------------
-// bf16, head_dim 128: the hot shape.  One workgroup = 4 waves x 64 queries (two
-// 32-query MFMA blocks per wave, so every K/V operand read from LDS feeds two
-// MFMAs).  Key tiles of 32 are prefetched into registers one step ahead and stored
-// into double-buffered, swizzled, row-major LDS tiles; V^T operands come from
-// transposing LDS reads, so V needs no transposition on the way in.  The loop is software-pipelined: the scores of tile t+1
-// are issued before the softmax of tile t, so the matrix cores work while the
-// vector ALUs do the softmax.
+// bf16, head_dim 128: the hot shape.  One workgroup = 4 waves x 32 queries of one
+// query head.  K and V tiles of 32 keys are copied global -> LDS (swizzled,
+// row-major) without staging registers into two rings of three slots, K three
+// tiles and V two tiles ahead of their use, so a copy has two steps to land.  V^T
+// operands come from transposing LDS reads.  The scores of tile t+1 are issued
+// before the softmax of tile t, so the matrix cores work while the vector ALUs do
+// the softmax.
 // ------------------------------------------------------------------------------------
-#ifndef RA_FWD_QB
-#define RA_FWD_QB 1  // 32-query MFMA blocks per wave
-#endif
-#ifndef RA_FWD_PIPE
-#define RA_FWD_PIPE 1  // issue the scores of tile t+1 before the softmax of tile t
-#endif
 constexpr int kD128Waves = 4;
 constexpr int kD128Threads = 64 * kD128Waves;
-constexpr int kD128QB = RA_FWD_QB;
-constexpr int kD128QW = 32 * kD128QB;             // queries per wave
-constexpr int kD128BM = kD128QW * kD128Waves;     // queries per workgroup
-constexpr int kD128BN = 32;                       // keys per tile
+constexpr int kD128BM = 32 * kD128Waves;  // queries per workgroup
+constexpr int kD128BN = 32;               // keys per tile
 
 template <bool kSeg>
 __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) {
-  constexpr int D = 128, BN = kD128BN, BM = kD128BM, QW = kD128QW, QB = kD128QB;
-  constexpr bool kPipe = RA_FWD_PIPE;
-  __shared__ __attribute__((aligned(1024))) __bf16 kbuf[2][BN * D];
-  __shared__ __attribute__((aligned(1024))) __bf16 vbuf[2][BN * D];
+  constexpr int D = 128, BN = kD128BN, BM = kD128BM;
+  // Each slot its own array, so the compiler can tell the copies in flight from
+  // the tiles being read.
+  __shared__ __attribute__((aligned(1024))) __bf16 ks0[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 ks1[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 ks2[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 vs0[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 vs1[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 vs2[BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -404,20 +401,14 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
 
   const int q0 = qt * BM;
   const int q_last = min(q0 + BM, a.Sq) - 1;
-  const int qw = q0 + wave * QW;
-  int qi[QB];
-  bool qv[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    qi[qb] = qw + 32 * qb + col;
-    qv[qb] = qi[qb] < a.Sq;
-  }
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + col;
+  const bool qv = qi < a.Sq;
 
-  const __bf16* qbase = static_cast<const __bf16*>(a.q);
-  const __bf16* kbase = static_cast<const __bf16*>(a.k) + (int64_t)b * a.Sk * a.Hkv * D + (int64_t)g * D;
-  const __bf16* vbase = static_cast<const __bf16*>(a.v) + (int64_t)b * a.Sk * a.Hkv * D + (int64_t)g * D;
   const int64_t q_rs = (int64_t)a.Hq * D;
-  const int64_t kv_rs = (int64_t)a.Hkv * D;
+  const int kv_rb = a.Hkv * D * 2;  // bytes between consecutive keys
+  const char* kbase = static_cast<const char*>(a.k) + ((int64_t)b * a.Sk * a.Hkv + g) * (D * 2);
+  const char* vbase = static_cast<const char*>(a.v) + ((int64_t)b * a.Sk * a.Hkv + g) * (D * 2);
 
   // Key tiles this workgroup visits.
   int n_keys = a.Sk;
@@ -427,15 +418,14 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
   }
   int kt_begin = 0, kt_end = (n_keys + BN - 1) / BN;
   const int32_t* seg_row = nullptr;
-  int seg_q[QB];
+  int seg_q = 0;
   int seg_w_lo = 0, seg_w_hi = 0;  // segment ids of the wave's first and last query
   if constexpr (kSeg) {
     seg_row = a.seg + (int64_t)b * a.seg_len;
     const int lo = seg_row[a.q_offset + q0], hi = seg_row[a.q_offset + q_last];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) seg_q[qb] = qv[qb] ? seg_row[a.q_offset + qi[qb]] : lo;
+    seg_q = qv ? seg_row[a.q_offset + qi] : lo;
     seg_w_lo = seg_row[a.q_offset + min(qw, a.Sq - 1)];
-    seg_w_hi = seg_row[a.q_offset + min(qw + QW, a.Sq) - 1];
+    seg_w_hi = seg_row[a.q_offset + min(qw + 32, a.Sq) - 1];
     const int32_t* seg_k = seg_row + a.kv_offset;
     int first_live = kt_end, last_live = -1;
     for (int base = 0; base < kt_end; base += 64) {
@@ -457,95 +447,80 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
   }
 
   // Q operands (B of S^T = K Q^T).
-  bf16x8 qf[QB][8];
+  bf16x8 qf[8];
+  {
+    const __bf16* qrow = static_cast<const __bf16*>(a.q) + ((int64_t)b * a.Sq + (qv ? qi : 0)) * q_rs +
+                         (int64_t)hq * D + 8 * half;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const __bf16* qrow = qbase + ((int64_t)b * a.Sq + (qv[qb] ? qi[qb] : 0)) * q_rs + (int64_t)hq * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[qb][s] = qv[qb] ? load_bf16x8(qrow + 16 * s) : bf16x8{};
+    for (int s = 0; s < 8; ++s) qf[s] = qv ? load_bf16x8(qrow + 16 * s) : bf16x8{};
   }
 
-  f32x16 oacc[QB][4];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[qb][db] = f32x16{};
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.0f;
+  // Causal limit: key k0 + 16*half + i is visible iff i <= causal_lim - k0.  Clamped
+  // to +-2^30 (k0 <= 2^30), which keeps the test exact without 64-bit arithmetic.
+  int causal_lim = 1 << 30;
+  if (a.causal) {
+    const int64_t c = a.q_offset + qi - a.kv_offset - 16 * half;
+    causal_lim = (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, c));
   }
-  f32x16 s_next[QB];
 
-  // Register prefetch of one 32-row tile: 512 chunks of 16 bytes, 2 per thread;
-  // 16 consecutive lanes read one 256-byte row (coalesced) and write it to the
-  // row's swizzled chunk positions (conflict-free).
-  u32x4 kreg[2], vreg[2];
-  auto fetch = [&](const __bf16* base, int t, u32x4* reg) {
+  // Copies: 32 rows x 256 bytes per tile = 8 blocks of 1 KiB, two per wave; lane
+  // l of a block writes 16 bytes at 16*l, so it fetches the global chunk that the
+  // swizzle puts there.  Raw buffer loads with a per-tile descriptor whose range
+  // ends at the chunk's last key: rows past it read as zeros (and are masked).
+  uint32_t coff[2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int u = tid + r * kD128Threads;
-      const int row = u >> 4, c = u & 15;
-      const int key = min(t * BN + row, a.Sk - 1);
-      reg[r] = *reinterpret_cast<const u32x4*>(base + (int64_t)key * kv_rs + c * 8);
-    }
-  };
-  auto put = [&](__bf16* tile, const u32x4* reg) {
+  for (int r = 0; r < 2; ++r) {
+    const int row = (2 * wave + r) * 4 + (lane >> 4);
+    coff[r] = (uint32_t)(row * kv_rb + ((lane & 15) ^ swz(row)) * 16);
+  }
+  auto copy_tile = [&](const char* base, int t, __bf16* dst) {
+    const int k0 = t * BN;
+    const int64_t bytes = (int64_t)(a.Sk - 1 - k0) * kv_rb + D * 2;  // through the last key's row
+    const buffer_rsrc rs = make_rsrc(base + (int64_t)k0 * kv_rb, bytes);
+    char* d = reinterpret_cast<char*>(dst) + 2 * wave * 1024;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int u = tid + r * kD128Threads;
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(tile) + tile_off(u >> 4, u & 15)) = reg[r];
-    }
+    for (int r = 0; r < 2; ++r) buffer_load_lds16(rs, d + r * 1024, coff[r]);
   };
-  // S^T of one key tile; each K operand feeds QB MFMAs.
-  auto qk = [&](const __bf16* ktile) {
+  constexpr int kCopiesPerTile = 2;  // per wave and tensor
+
+  // LDS operand offsets.  K (A of S^T): row key_of_row(col), 16-byte chunk 2s+half,
+  // i.e. kA ^ (s << 5).  V^T (A of O^T += V^T P^T) via transposing reads of rows
+  // 16*half + 8m + k (+4) at columns 32*db + ...: two per-lane bases, the rest is
+  // immediate (the swizzle of these rows does not depend on m or db).
+  const int krow = key_of_row(col);
+  const int kA = krow * 256 + 32 * (krow & 7) + 16 * (half ^ ((krow >> 4) & 1));
+  int v_even, v_odd;
+  {
+    const int s16 = lane & 15, mm = s16 & 3, kk = s16 >> 2;
+    const int x = (2 * ((lane >> 4) & 1) + (mm >> 1)) ^ (2 * kk + half);
+    const int base = 4096 * half + 256 * kk + 16 * (x & 3) + 8 * (mm & 1);
+    v_even = base + 64 * (x >> 2);
+    v_odd = base - 64 * (x >> 2);
+  }
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  auto tr_read = [](const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
+  };
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  auto qk = [&](const __bf16* kt) {
+    const char* base = reinterpret_cast<const char*>(kt);
     bf16x8 kf[8];
-    const int row = key_of_row(col);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kf[s] = read_chunk(ktile, row, 2 * s + half);
-    if constexpr (RA_FWD_BATCH) __builtin_amdgcn_sched_barrier(0);  // all K reads in flight before the first MFMA
+    for (int s = 0; s < 8; ++s) kf[s] = load_bf16x8(base + (kA ^ (s << 5)));
+    __builtin_amdgcn_sched_barrier(0);  // all eight reads in flight before the first MFMA
+    f32x16 acc = f32x16{};
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s_next[qb] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s_next[qb] = mfma_bf16(kf[s], qf[qb][s], s_next[qb]);
+    for (int s = 0; s < 8; ++s) acc = mfma_bf16(kf[s], qf[s], acc);
+    return acc;
   };
 
-  if (kt_begin < kt_end) {
-    fetch(kbase, kt_begin, kreg);
-    fetch(vbase, kt_begin, vreg);
-    put(kbuf[0], kreg);
-    put(vbuf[0], vreg);
-    if (kPipe && kt_begin + 1 < kt_end) {
-      fetch(kbase, kt_begin + 1, kreg);
-      put(kbuf[1], kreg);
-    }
-    __syncthreads();
-    if constexpr (kPipe) qk(kbuf[0]);
-  }
-  for (int t = kt_begin; t < kt_end; ++t) {
-    const int cur = (t - kt_begin) & 1;
-    __syncthreads();  // tiles of this step visible; every wave is done with step t-1 (or the prologue)
-    const bool more1 = t + 1 < kt_end, more2 = t + 2 < kt_end;
-    f32x16 sc[QB];
-    if constexpr (kPipe) {
-      if (more2) fetch(kbase, t + 2, kreg);
-      if (more1) fetch(vbase, t + 1, vreg);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[qb] = s_next[qb];
-      if (more1) qk(kbuf[cur ^ 1]);
-    } else {
-      if (more1) {
-        fetch(kbase, t + 1, kreg);
-        fetch(vbase, t + 1, vreg);
-      }
-      qk(kbuf[cur]);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[qb] = s_next[qb];
-    }
-
+  // Softmax of tile t's scores and O^T += V^T P^T.
+  auto consume = [&](f32x16 sc, const __bf16* vt, int t) {
     const int k0 = t * BN;
     bool partial = (k0 + BN > a.Sk);
     if (a.causal) partial |= (a.kv_offset + k0 + BN - 1 > a.q_offset + qw);
@@ -556,111 +531,142 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
       const int sk_hi = seg_row[a.kv_offset + min(k0 + BN, a.Sk) - 1];
       partial |= !(sk_lo == sk_hi && sk_lo == seg_w_lo && seg_w_lo == seg_w_hi);
     }
-    if (partial) {
-      // Per-element visibility: key index of register i in half h is k0 + 16h + i.
-      int segk[16];
+    if (partial) {  // one wave-uniform branch around the element mask
+      // Register i of half h holds key k0 + 16h + i.
+      const int lim = min(a.causal ? causal_lim - k0 : (1 << 30), a.Sk - 1 - k0 - 16 * half);
       if constexpr (kSeg) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int kj = k0 + 16 * half + i;
-          segk[i] = kj < a.Sk ? seg_row[a.kv_offset + kj] : INT32_MIN;
+          // Wave-uniform addresses (scalar loads), clamped into the chunk.
+          const int s_lo = seg_row[a.kv_offset + min(k0 + i, a.Sk - 1)];
+          const int s_hi = seg_row[a.kv_offset + min(k0 + 16 + i, a.Sk - 1)];
+          const bool vis = (i <= lim) & ((half ? s_hi : s_lo) == seg_q);
+          sc[i] = vis ? sc[i] : -INFINITY;
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = (i <= lim) ? sc[i] : -INFINITY;
       }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kj = k0 + 16 * half + i;
-          bool vis = kj < a.Sk;
-          if (a.causal) vis = vis && (a.kv_offset + kj <= a.q_offset + qi[qb]);
-          if constexpr (kSeg) vis = vis && (segk[i] == seg_q[qb]);
-          sc[qb][i] = vis ? sc[qb][i] : -INFINITY;
-        }
     }
 
-    float tmax[QB];
-    bool grow[QB];
-    bool any_grow = false;
+    float r = sc[0];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float r = sc[qb][0];
+    for (int i = 1; i < 16; ++i) r = fmaxf(r, sc[i]);
+    const float tmax = half_max(r) * a.scale_log2;
+    // Lazy rescaling: the running max only moves when a row's max grows by more
+    // than kSlack (log2 units), so P stays <= 2^kSlack and most tiles skip the
+    // rescale of O entirely.  Both halves of a row see the same tmax and m_run.
+    const bool grow = tmax > m_run + kSlack;
+    if (__ballot(grow)) {
+      const float al = grow ? exp2_fast(m_run - tmax) : 1.0f;  // 0 when m_run = -inf
+      if (grow) m_run = tmax;
+      l_run *= al;
 #pragma unroll
-      for (int i = 1; i < 16; ++i) r = fmaxf(r, sc[qb][i]);
-      r = fmaxf(r, __shfl_xor(r, 32));
-      tmax[qb] = r * a.scale_log2;
-      grow[qb] = tmax[qb] > m_run[qb] + kSlack;
-      any_grow |= grow[qb];
+      for (int db = 0; db < 4; ++db) oacc[db] *= al;
     }
-    if (__ballot(any_grow)) {
+    const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
+    float p[16];
+    float psum = 0.0f;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float al = grow[qb] ? exp2_fast(m_run[qb] - tmax[qb]) : 1.0f;
-        if (grow[qb]) m_run[qb] = tmax[qb];
-        l_run[qb] *= al;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[qb][db] *= al;
-      }
+    for (int i = 0; i < 16; ++i) {
+      p[i] = exp2_fast(__builtin_fmaf(sc[i], a.scale_log2, neg_m));
+      psum += p[i];
     }
-    bf16x8 pf[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float neg_m = (m_run[qb] == -INFINITY) ? 0.0f : -m_run[qb];
-      float p[16];
-      float psum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = exp2_fast(__builtin_fmaf(sc[qb][i], a.scale_log2, neg_m));
-        psum += p[i];
-      }
-      l_run[qb] += psum;
-      pf[qb][0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-      pf[qb][1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-    }
+    l_run += psum;
+    const bf16x8 pf0 = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    const bf16x8 pf1 = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+
     // O^T += V^T P^T: register 8m+j of half h holds key 16h + 8m + j.
-    const __bf16* vread = vbuf[cur];
+    const char* vb = reinterpret_cast<const char*>(vt);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       bf16x8 vf[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) vf[db] = read_transposed(vread, 16 * half + 8 * m, 32 * db, lane);
-      if constexpr (RA_FWD_BATCH) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma_bf16(vf[db], pf[qb][m], oacc[qb][db]);
-    }
-    if constexpr (kPipe) {
-      // K(t+2) replaces K(t) (read during step t-1); V(t+1) replaces V(t-1).
-      if (more2) put(kbuf[cur], kreg);
-      if (more1) put(vbuf[cur ^ 1], vreg);
-    } else {
-      // Other waves may still read this step's tiles: the next step's barrier
-      // orders these stores after them (the tiles go to the other slot).
-      if (more1) {
-        put(kbuf[cur ^ 1], kreg);
-        put(vbuf[cur ^ 1], vreg);
+      for (int db = 0; db < 4; ++db) {
+        const char* p0 = vb + ((db & 1) ? v_odd : v_even) + 64 * db + 2048 * m;
+        const bf16x4_t x0 = tr_read(p0);
+        const bf16x4_t x1 = tr_read(p0 + 1024 + (db < 2 ? 128 : -128));
+        vf[db] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] = mfma_bf16(vf[db], m ? pf1 : pf0, oacc[db]);
+    }
+  };
+
+  // One step: K(t+1) and V(t) must have landed (copied two steps ago; this wave's
+  // copies from the previous step may stay in flight), then every wave's copies are
+  // published with a bare s_barrier (a workgroup fence would also drain the copies
+  // in flight; the empty asm statements keep LDS accesses on their side of it).
+  // The slots freed by that barrier receive K(t+3) and V(t+2).
+  f32x16 s_next = f32x16{};
+  auto step = [&](int t, const __bf16* kq, const __bf16* vc, __bf16* kn, __bf16* vn) {
+    if (t + 2 < kt_end)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kCopiesPerTile));  // vmcnt(4)
+    else if (t + 1 < kt_end)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesPerTile);  // vmcnt(2)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 3 < kt_end) copy_tile(kbase, t + 3, kn);
+    if (t + 2 < kt_end) copy_tile(vbase, t + 2, vn);
+    // Scores of tile t+1 (on the last step the slot is stale and the result unused).
+    const f32x16 sc = s_next;
+    s_next = qk(kq);
+    consume(sc, vc, t);
+  };
+
+  if (kt_begin < kt_end) {
+    const int t = kt_begin;
+    copy_tile(kbase, t, ks0);
+    copy_tile(vbase, t, vs0);
+    if (t + 1 < kt_end) {
+      copy_tile(kbase, t + 1, ks1);
+      copy_tile(vbase, t + 1, vs1);
+    }
+    if (t + 2 < kt_end) copy_tile(kbase, t + 2, ks2);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    s_next = qk(ks0);
+  }
+  // Slots: K(j) in ks[(j - kt_begin) % 3], V(j) in vs[(j - kt_begin) % 3].  Six
+  // steps per iteration, so the two score register sets alternate without copies;
+  // every exit leaves through a break, so only O, m and l are live there.
+  if (kt_begin < kt_end) {
+    for (int t = kt_begin;; t += 6) {
+      step(t, ks1, vs0, ks0, vs2);
+      if (t + 1 >= kt_end) break;
+      step(t + 1, ks2, vs1, ks1, vs0);
+      if (t + 2 >= kt_end) break;
+      step(t + 2, ks0, vs2, ks2, vs1);
+      if (t + 3 >= kt_end) break;
+      step(t + 3, ks1, vs0, ks0, vs2);
+      if (t + 4 >= kt_end) break;
+      step(t + 4, ks2, vs1, ks1, vs0);
+      if (t + 5 >= kt_end) break;
+      step(t + 5, ks0, vs2, ks2, vs1);
+      if (t + 6 >= kt_end) break;
     }
   }
 
+  const float l_tot = half_sum(l_run);
+  const bool live = l_tot > 0.0f;
+  const float inv = live ? 1.0f / l_tot : 0.0f;
+  if (qv) {
+    float* orow = a.o + ((int64_t)b * a.Sq + qi) * q_rs + (int64_t)hq * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    const bool live = l_tot > 0.0f;
-    const float inv = live ? 1.0f / l_tot : 0.0f;
-    if (qv[qb]) {
-      float* orow = a.o + ((int64_t)b * a.Sq + qi[qb]) * q_rs + (int64_t)hq * D;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          f32x4 v = {oacc[qb][db][4 * r4] * inv, oacc[qb][db][4 * r4 + 1] * inv, oacc[qb][db][4 * r4 + 2] * inv,
-                     oacc[qb][db][4 * r4 + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * half) = v;
-        }
-      if (half == 0)
-        a.lse[((int64_t)b * a.Hq + hq) * a.Sq + qi[qb]] = live ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
-    }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v = {oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv, oacc[db][4 * r4 + 2] * inv,
+                   oacc[db][4 * r4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * half) = v;
+      }
+    if (half == 0)
+      a.lse[((int64_t)b * a.Hq + hq) * a.Sq + qi] = live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 

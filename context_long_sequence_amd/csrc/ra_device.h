@@ -115,6 +115,29 @@ __device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >>
 
 __device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
 
+// Combines the two half-waves: lane l and lane l^32 both get op(x[l mod 32],
+// x[32 + l mod 32]) (v_permlane32_swap: one VALU op, no LDS round trip).
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Raw buffer resource (gfx9 layout: stride 0, range checked per byte offset).
+// Loads whose 16 bytes end past `bytes` return zeros instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc;
+__device__ __forceinline__ buffer_rsrc make_rsrc(const void* base, int64_t bytes) {
+  const int n = (int)(bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+// 16 bytes per lane from base + voffset into LDS at dst + 16*lane (dst wave-uniform).
+__device__ __forceinline__ void buffer_load_lds16(buffer_rsrc rs, void* dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, voffset, 0, 0, 0);
+}
+
 // Wait until every global->LDS load issued by this wave has landed.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

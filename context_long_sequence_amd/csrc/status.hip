@@ -32,6 +32,11 @@ ra_status validate_step(const ra_shape* s, const int32_t* seg_ids, int64_t seg_l
   if (s->batch < 1 || s->q_len < 1 || s->kv_len < 1)
     return fail(RA_ERR_INVALID_ARGUMENT, "batch, q_len and kv_len must be >= 1 (got %d, %d, %d)",
                 s->batch, s->q_len, s->kv_len);
+  // Tile arithmetic inside the kernels is 32-bit, and per-lane byte offsets within
+  // a tile of rows are 32-bit.
+  if (s->q_len > (1 << 30) || s->kv_len > (1 << 30))
+    return fail(RA_ERR_INVALID_ARGUMENT, "q_len and kv_len must be <= 2^30 (got %d, %d)", s->q_len, s->kv_len);
+  if (s->heads_q > 4096) return fail(RA_ERR_INVALID_ARGUMENT, "heads_q must be <= 4096 (got %d)", s->heads_q);
   if (s->heads_q < 1 || s->heads_kv < 1 || s->heads_q % s->heads_kv != 0)
     return fail(RA_ERR_INVALID_ARGUMENT, "heads_q (%d) must be a positive multiple of heads_kv (%d)",
                 s->heads_q, s->heads_kv);

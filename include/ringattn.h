@@ -59,9 +59,9 @@ typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype;
 /* Shape and mask of one ring step: the local query shard against one KV chunk. */
 typedef struct {
   int32_t batch;     /* B >= 1 */
-  int32_t q_len;     /* Sq >= 1: rows of the local query shard */
-  int32_t kv_len;    /* Sk >= 1: keys of this chunk */
-  int32_t heads_q;   /* Hq >= 1, a multiple of heads_kv */
+  int32_t q_len;     /* 1 <= Sq <= 2^30: rows of the local query shard */
+  int32_t kv_len;    /* 1 <= Sk <= 2^30: keys of this chunk */
+  int32_t heads_q;   /* 1 <= Hq <= 4096, a multiple of heads_kv */
   int32_t heads_kv;  /* Hkv >= 1 */
   int32_t head_dim;  /* d: 64 or 128 */
   int64_t q_offset;  /* global token index of query row 0 (rank * chunk length) */
@@ -89,8 +89,8 @@ typedef struct {
  *           Ids that decrease along a row give unspecified values (never an
  *           out-of-bounds access).
  *  o_step   [B, Sq, Hq, d] fp32 out;  lse_step [B, Hq, Sq] fp32 out (natural log).
- * Errors: RA_ERR_INVALID_ARGUMENT for NULL q/k/v/o_step/lse_step, sizes < 1,
- * Hq % Hkv != 0, negative offsets, seg ranges past seg_len, misaligned pointers;
+ * Errors: RA_ERR_INVALID_ARGUMENT for NULL q/k/v/o_step/lse_step, sizes < 1
+ * or above the ra_shape limits, Hq % Hkv != 0, negative offsets, seg ranges past seg_len, misaligned pointers;
  * RA_ERR_UNSUPPORTED for head_dim not in {64, 128} or an unknown dtype.
  */
 ra_status ring_attn_fwd_step(const ra_shape* shape, const void* q, const void* k, const void* v,
