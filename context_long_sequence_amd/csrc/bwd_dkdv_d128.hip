@@ -4,13 +4,13 @@
 // final log-sum-exp (archcrux, "sequence-parallel long-context attention OOM").
 // Each wave keeps 32 keys' K and V operands and dK/dV accumulators in registers
 // and walks the 64-query tiles of every query head of the group.  Q and dO tiles
-// are copied global -> LDS (swizzled, row-major) two steps ahead into a ring of
-// three slots without passing through registers; their transposes are read with
-// transposing LDS reads.
+// are copied global -> LDS (swizzled, row-major; raw buffer loads, no staging
+// registers) two steps ahead into a ring of three slots; their transposes are
+// read with transposing LDS reads.
 #include "bwd_d128.h"
 
-#ifndef RA_DKDV_BATCH
-#define RA_DKDV_BATCH 1  // issue each MFMA chain's operand reads before its first MFMA
+#ifndef RA_DKDV_SCHED
+#define RA_DKDV_SCHED 0
 #endif
 
 namespace ra {
@@ -41,7 +41,8 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) float xs1[4 * QT];
   __shared__ __attribute__((aligned(1024))) float xs2[4 * QT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
   const int kt = logical % a.n_tiles;
   const int g = (logical / a.n_tiles) % a.Hkv;
@@ -56,6 +57,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   const int64_t kgl = a.kv_offset + kj;
 
   const int64_t q_rs = (int64_t)a.Hq * kD, kv_rs = (int64_t)a.Hkv * kD;
+  const int q_rb = a.Hq * kD * 2;  // bytes between consecutive query rows
 
   // K and V of this lane's key as B operands of S = Q K^T and dP = dO V^T.
   bf16x8 kf[8], vf[8];
@@ -93,6 +95,13 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   const int n_q = qt_end - qt_begin;
   const int n_iter = n_q * group;
 
+  // Visibility of query q0 + 16*half + i to this lane's key: lo - q0 <= i < hi - q0
+  // (causal rule and the end of the query shard; 32-bit: offsets clamped to +-2^30,
+  // q0 <= 2^30).  A key past the chunk end sees nothing.
+  int vis_lo = -(1 << 30), vis_hi = a.Sq - 16 * half;
+  if (a.causal) vis_lo = (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, kgl - a.q_offset - 16 * half));
+  if (!k_valid) vis_hi = -(1 << 30);
+
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
@@ -100,104 +109,340 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     dv[db] = f32x16{};
   }
 
-  const __bf16* qg_base = static_cast<const __bf16*>(a.q) + (int64_t)b * a.Sq * q_rs;
-  const __bf16* dg_base = static_cast<const __bf16*>(a.d_o) + (int64_t)b * a.Sq * q_rs;
+  const char* qg_base = static_cast<const char*>(a.q) + (int64_t)b * a.Sq * q_rs * 2;
+  const char* dg_base = static_cast<const char*>(a.d_o) + (int64_t)b * a.Sq * q_rs * 2;
 
-  // Copies tile t (query head, 64 queries) global -> LDS slot without registers:
-  // 4 + 4 sixteen-byte copies of Q/dO rows and one 4-byte-per-lane copy of
-  // lse (wave 0), delta (wave 1), segment ids (wave 2) or a dummy (wave 3).
+  // Copies of tile t (query head, 64 queries) global -> LDS slot, no staging
+  // registers: 64 rows x 256 bytes per tensor = 16 blocks of 1 KiB, four per wave
+  // (lane l of a block writes 16 bytes at 16*l, so it fetches the global chunk the
+  // swizzle puts there), plus one 4-byte-per-lane copy of lse (wave 0), delta
+  // (wave 1), segment ids (wave 2) or a dummy (wave 3).  Raw buffer loads with
+  // per-tile descriptors ending at the shard's last query: rows past it read as
+  // zeros (and are masked).
+  uint32_t coff[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = (4 * wave + r) * 4 + (lane >> 4);
+    coff[r] = (uint32_t)(row * q_rb + ((lane & 15) ^ swz(row)) * 16);
+  }
   auto issue = [&](int t, __bf16* qs, __bf16* ds, float* xs) {
     const int hq = g * group + t / n_q;
     const int q0 = (qt_begin + t % n_q) * QT;
-    const int64_t hoff = (int64_t)hq * kD + (int64_t)q0 * q_rs;
-    load_rows_lds<QT, 4>(qs, qg_base + hoff, q_rs, a.Sq - q0, wave, lane);
-    load_rows_lds<QT, 4>(ds, dg_base + hoff, q_rs, a.Sq - q0, wave, lane);
-    const int qi = min(q0 + lane, a.Sq - 1);
-    const int64_t li = ((int64_t)b * a.Hq + hq) * a.Sq + qi;
+    const int64_t hoff = (int64_t)q0 * q_rb + (int64_t)hq * (kD * 2);
+    const int64_t bytes = (int64_t)(a.Sq - 1 - q0) * q_rb + kD * 2;
+    const buffer_rsrc rq = make_rsrc(qg_base + hoff, bytes);
+    const buffer_rsrc rd = make_rsrc(dg_base + hoff, bytes);
+    char* dq_ = reinterpret_cast<char*>(qs) + 4 * wave * 1024;
+    char* dd_ = reinterpret_cast<char*>(ds) + 4 * wave * 1024;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) buffer_load_lds16(rq, dq_ + r * 1024, coff[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) buffer_load_lds16(rd, dd_ + r * 1024, coff[r]);
+    const int64_t li = ((int64_t)b * a.Hq + hq) * a.Sq + q0;
     const void* src = a.lse + li;
     if (wave == 1) src = a.delta + li;
     if constexpr (kSeg) {
-      if (wave == 2) src = seg_row + a.q_offset + qi;
+      if (wave == 2) src = seg_row + a.q_offset + q0;
     }
-    __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(xs + wave * QT), 4, 0, 0);
+    buffer_load_lds4(make_rsrc(src, (int64_t)(a.Sq - q0) * 4), xs + wave * QT, (uint32_t)lane * 4);
   };
   constexpr int kCopiesPerTile = 9;
   static_assert(kCopiesPerTile == 2 * (QT / 4 / 4) + 1, "copy count per wave and tile");
 
+  // LDS operand offsets.  Q and dO rows (A of S = Q K^T, dP = dO V^T): row
+  // 32*qb + key_of_row(col), 16-byte chunk 2c+half, i.e. 8192*qb + (rA ^ (c << 5)).
+  // dO^T and Q^T (B of dV += P^T dO, dK += dS^T Q) by transposing reads of rows
+  // 32*qb + 16*half + 8m + k (+4): two per-lane bases, the rest immediate.
+  const int rrow = key_of_row(col);
+  const int rA = rrow * 256 + 32 * (rrow & 7) + 16 * (half ^ ((rrow >> 4) & 1));
+  int t_even, t_odd;
+  {
+    const int s16 = lane & 15, mm = s16 & 3, kk = s16 >> 2;
+    const int x = (2 * ((lane >> 4) & 1) + (mm >> 1)) ^ (2 * kk + half);
+    const int base = 4096 * half + 256 * kk + 16 * (x & 3) + 8 * (mm & 1);
+    t_even = base + 64 * (x >> 2);
+    t_odd = base - 64 * (x >> 2);
+  }
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  auto tr_read = [](const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
+  };
+
+  // One 64-query tile against the wave's 32 keys, as two 32-query blocks in one
+  // straight-line body: the scores of both blocks first, then per block the
+  // softmax and the dV/dK products, so the scheduler can overlap one block's vector
+  // work with the other block's MFMAs.  P uses the final LSE as is: a query whose
+  // LSE is -inf sees no key at all, so its elements are masked in every block that
+  // holds it.  The bounds mask is applied to every block (it also zeroes blocks
+  // that lie entirely before the wave's keys); the segment test only where needed.
   auto compute = [&](int it, const __bf16* qt_, const __bf16* dt_, const float* xs) {
     const int qtile0 = (qt_begin + it % n_q) * QT;
+    const char* qc = reinterpret_cast<const char*>(qt_);
+    const char* dc = reinterpret_cast<const char*>(dt_);
+    // S = Q K^T and dP = dO V^T: lane = key, register i of half h = query q0 + 16h + i.
+    f32x16 s[2], dp[2];
+    bf16x8 fq[2][8], fd[2][8];
+    auto read_ops = [&](int qb) {
 #pragma unroll
-    for (int qb = 0; qb < QT / 32; ++qb) {
+      for (int c = 0; c < 8; ++c) {
+        fq[qb][c] = load_bf16x8(qc + 8192 * qb + (rA ^ (c << 5)));
+        fd[qb][c] = load_bf16x8(dc + 8192 * qb + (rA ^ (c << 5)));
+      }
+    };
+    auto score_mfmas = [&](int qb) {
+      s[qb] = f32x16{};
+      dp[qb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        s[qb] = mfma_bf16(fq[qb][c], kf[c], s[qb]);
+        dp[qb] = mfma_bf16(fd[qb][c], vf[c], dp[qb]);
+      }
+    };
+    // Softmax-side vector work of block qb: P and dS as bf16 MFMA operands.
+    bf16x8 pf[2][2], sf[2][2];
+    auto softmax = [&](int qb) {
       const int q0 = qtile0 + 32 * qb;
-      bool partial = (q0 + 32 > a.Sq) || (kw + 32 > a.Sk);  // wave-uniform
-      if (a.causal) partial |= (a.kv_offset + kw + 31 > a.q_offset + q0);
+      const float* lse_q = xs + 32 * qb + 16 * half;
+      const float* del_q = xs + QT + 32 * qb + 16 * half;
+      float p[16], dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(s[qb][i], a.scale_log2, lse_q[i] * -kLog2e));
+      {
+        const int lo = vis_lo - q0, hi = vis_hi - q0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = ((i >= lo) & (i < hi)) ? p[i] : 0.0f;
+      }
       if constexpr (kSeg) {
         // Segment ids are nondecreasing: only blocks that straddle a segment
         // boundary need the per-element segment test.
         const int sq_lo = __builtin_bit_cast(int, xs[2 * QT + 32 * qb]);
         const int sq_hi = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 31]);
-        partial |= !(sq_lo == sq_hi && sq_lo == seg_w_lo && seg_w_lo == seg_w_hi);
-      }
-      if (a.causal && a.kv_offset + kw > a.q_offset + q0 + 31) continue;  // block entirely before these keys
-
-      // S = Q K^T and dP = dO V^T: lane = key, register i of half h = query q0 + 16h + i.
-      f32x16 s = f32x16{}, dp = f32x16{};
-      {
-        const int row = 32 * qb + key_of_row(col);
-        bf16x8 fq[8], fd[8];
+        if (!(sq_lo == sq_hi && sq_lo == seg_w_lo && seg_w_lo == seg_w_hi)) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) fq[c] = read_chunk(qt_, row, 2 * c + half);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) fd[c] = read_chunk(dt_, row, 2 * c + half);
-        if constexpr (RA_DKDV_BATCH) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          s = mfma_bf16(fq[c], kf[c], s);
-          dp = mfma_bf16(fd[c], vf[c], dp);
-        }
-      }
-      float p[16], dsv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float l = xs[32 * qb + 16 * half + i];
-        // a row with no visible key at all (LSE = -inf) contributes nothing
-        const float neg_lse2 = l == -INFINITY ? -INFINITY : -l * kLog2e;
-        p[i] = exp2_fast(__builtin_fmaf(s[i], a.scale_log2, neg_lse2));
-      }
-      if (partial) {  // one wave-uniform branch around the element mask
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = 32 * qb + 16 * half + i;
-          const int qi = qtile0 + ql;
-          bool vis = qi < a.Sq && k_valid;
-          if (a.causal) vis = vis && (kgl <= a.q_offset + qi);
-          if constexpr (kSeg) vis = vis && (__builtin_bit_cast(int, xs[2 * QT + ql]) == seg_k);
-          p[i] = vis ? p[i] : 0.0f;
+          for (int i = 0; i < 16; ++i)
+            p[i] = (__builtin_bit_cast(int, xs[2 * QT + 32 * qb + 16 * half + i]) == seg_k) ? p[i] : 0.0f;
         }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dsv[i] = p[i] * (dp[i] - xs[QT + 32 * qb + 16 * half + i]);
-      // dV += P^T dO and dK += dS^T Q; dO^T / Q^T operands by transposing reads.
+      for (int i = 0; i < 16; ++i) dsv[i] = p[i] * (dp[qb][i] - del_q[i]);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const bf16x8 pf = to_bf16x8(p[8 * m], p[8 * m + 1], p[8 * m + 2], p[8 * m + 3], p[8 * m + 4], p[8 * m + 5],
-                                    p[8 * m + 6], p[8 * m + 7]);
-        const bf16x8 sf = to_bf16x8(dsv[8 * m], dsv[8 * m + 1], dsv[8 * m + 2], dsv[8 * m + 3], dsv[8 * m + 4],
-                                    dsv[8 * m + 5], dsv[8 * m + 6], dsv[8 * m + 7]);
-        bf16x8 dot[4], qtf[4];
+        pf[qb][m] = to_bf16x8(p[8 * m], p[8 * m + 1], p[8 * m + 2], p[8 * m + 3], p[8 * m + 4], p[8 * m + 5],
+                              p[8 * m + 6], p[8 * m + 7]);
+        sf[qb][m] = to_bf16x8(dsv[8 * m], dsv[8 * m + 1], dsv[8 * m + 2], dsv[8 * m + 3], dsv[8 * m + 4],
+                              dsv[8 * m + 5], dsv[8 * m + 6], dsv[8 * m + 7]);
+      }
+    };
+    // dO^T and Q^T operands of block qb (transposing reads), then dV += P^T dO, dK += dS^T Q.
+    bf16x8 dot[2][2][4], qtf[2][2][4];
+    auto read_tr = [&](int qb, int m) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          dot[db] = read_transposed(dt_, 32 * qb + 16 * half + 8 * m, 32 * db, lane);
-          qtf[db] = read_transposed(qt_, 32 * qb + 16 * half + 8 * m, 32 * db, lane);
-        }
-        if constexpr (RA_DKDV_BATCH) __builtin_amdgcn_sched_barrier(0);
+      for (int db = 0; db < 4; ++db) {
+        const int o = ((db & 1) ? t_odd : t_even) + 64 * db + 2048 * m + 8192 * qb;
+        const int o1 = o + 1024 + (db < 2 ? 128 : -128);
+        const bf16x4_t d0 = tr_read(dc + o), d1 = tr_read(dc + o1);
+        const bf16x4_t q0v = tr_read(qc + o), q1v = tr_read(qc + o1);
+        dot[qb][m][db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        qtf[qb][m][db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
+      }
+    };
+    auto grad_mfmas = [&](int qb, int m) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          dv[db] = mfma_bf16(pf, dot[db], dv[db]);
-          dk[db] = mfma_bf16(sf, qtf[db], dk[db]);
-        }
+      for (int db = 0; db < 4; ++db) {
+        dv[db] = mfma_bf16(pf[qb][m], dot[qb][m][db], dv[db]);
+        dk[db] = mfma_bf16(sf[qb][m], qtf[qb][m][db], dk[db]);
+      }
+    };
+#if RA_DKDV_SCHED == 1
+    // Each MFMA chain's operand reads issued as a batch before its first MFMA.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      read_ops(qb);
+      __builtin_amdgcn_sched_barrier(0);
+      score_mfmas(qb);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      softmax(qb);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        read_tr(qb, m);
+        __builtin_amdgcn_sched_barrier(0);
+        grad_mfmas(qb, m);
       }
     }
+#elif RA_DKDV_SCHED == 2
+    // Explicit pipeline: block 1's operand reads under block 0's score MFMAs; block
+    // 0's softmax and transposed reads under block 1's score MFMAs; block 1's
+    // softmax and transposed reads under block 0's gradient MFMAs.
+    read_ops(0);
+    __builtin_amdgcn_sched_barrier(0);
+    score_mfmas(0);
+    read_ops(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    score_mfmas(1);
+    softmax(0);
+    read_tr(0, 0);
+    read_tr(0, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    grad_mfmas(0, 0);
+    grad_mfmas(0, 1);
+    softmax(1);
+    read_tr(1, 0);
+    read_tr(1, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 2);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    grad_mfmas(1, 0);
+    grad_mfmas(1, 1);
+#elif RA_DKDV_SCHED == 3
+    // Hand-placed pipeline, pinned with scheduling fences: each MFMA slot (32 clocks)
+    // carries one element of the other block's softmax and a few LDS reads, so one
+    // wave keeps the matrix core busy while its vector ALU works.
+    float lq[2][16], dq_[2][16];
+    auto read_rows = [&](int qb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        lq[qb][i] = xs[32 * qb + 16 * half + i] * -kLog2e;
+        dq_[qb][i] = xs[QT + 32 * qb + 16 * half + i];
+      }
+    };
+    float p0[16], ds0[16];
+    auto element = [&](int qb, int i, float* pp, float* dd) {
+      const int q0 = qtile0 + 32 * qb;
+      float pv = exp2_fast(__builtin_fmaf(s[qb][i], a.scale_log2, lq[qb][i]));
+      pv = ((i >= vis_lo - q0) & (i < vis_hi - q0)) ? pv : 0.0f;
+      float dv_ = pv * (dp[qb][i] - dq_[qb][i]);
+      // Pin the element to its slot: the empty statement is ordered with the
+      // scheduling fences, so the arithmetic cannot sink towards its later use.
+      asm volatile("" : "+v"(pv), "+v"(dv_));
+      pp[i] = pv;
+      dd[i] = dv_;
+    };
+    auto seg_fix = [&](int qb, float* pp, float* dd) {
+      if constexpr (kSeg) {
+        const int sq_lo = __builtin_bit_cast(int, xs[2 * QT + 32 * qb]);
+        const int sq_hi = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 31]);
+        if (!(sq_lo == sq_hi && sq_lo == seg_w_lo && seg_w_lo == seg_w_hi)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const bool ok = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 16 * half + i]) == seg_k;
+            pp[i] = ok ? pp[i] : 0.0f;
+            dd[i] = ok ? dd[i] : 0.0f;
+          }
+        }
+      }
+    };
+    auto pack = [&](int qb, const float* pp, const float* dd) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        pf[qb][m] = to_bf16x8(pp[8 * m], pp[8 * m + 1], pp[8 * m + 2], pp[8 * m + 3], pp[8 * m + 4], pp[8 * m + 5],
+                              pp[8 * m + 6], pp[8 * m + 7]);
+        sf[qb][m] = to_bf16x8(dd[8 * m], dd[8 * m + 1], dd[8 * m + 2], dd[8 * m + 3], dd[8 * m + 4],
+                              dd[8 * m + 5], dd[8 * m + 6], dd[8 * m + 7]);
+      }
+    };
+    auto tr_one = [&](int qb, int m, int db) {
+      const int o = ((db & 1) ? t_odd : t_even) + 64 * db + 2048 * m + 8192 * qb;
+      const int o1 = o + 1024 + (db < 2 ? 128 : -128);
+      const bf16x4_t d0 = tr_read(dc + o), d1 = tr_read(dc + o1);
+      const bf16x4_t q0v = tr_read(qc + o), q1v = tr_read(qc + o1);
+      dot[qb][m][db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      qtf[qb][m][db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
+    };
+    // P0: block 0 operands and row scalars.
+    read_ops(0);
+    read_rows(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // P1: block 0 scores; block 1 operand reads in their shadow.
+    s[0] = f32x16{};
+    dp[0] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      s[0] = mfma_bf16(fq[0][c], kf[c], s[0]);
+      fq[1][c] = load_bf16x8(qc + 8192 + (rA ^ (c << 5)));
+      __builtin_amdgcn_sched_barrier(0);
+      dp[0] = mfma_bf16(fd[0][c], vf[c], dp[0]);
+      fd[1][c] = load_bf16x8(dc + 8192 + (rA ^ (c << 5)));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    read_rows(1);
+    __builtin_amdgcn_sched_barrier(0);
+    // P2: block 1 scores; block 0 softmax and block 0 transposed reads (m = 0).
+    s[1] = f32x16{};
+    dp[1] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      s[1] = mfma_bf16(fq[1][c], kf[c], s[1]);
+      element(0, 2 * c, p0, ds0);
+      if (c < 4) tr_one(0, 0, c);
+      __builtin_amdgcn_sched_barrier(0);
+      dp[1] = mfma_bf16(fd[1][c], vf[c], dp[1]);
+      element(0, 2 * c + 1, p0, ds0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    seg_fix(0, p0, ds0);
+    pack(0, p0, ds0);
+    __builtin_amdgcn_sched_barrier(0);
+    // P3: block 0 gradients; block 1 softmax and the remaining transposed reads.
+    float p1[16], ds1[16];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        dv[db] = mfma_bf16(pf[0][m], dot[0][m][db], dv[db]);
+        element(1, 8 * m + 2 * db, p1, ds1);
+        if (m == 0) tr_one(0, 1, db);
+        __builtin_amdgcn_sched_barrier(0);
+        dk[db] = mfma_bf16(sf[0][m], qtf[0][m][db], dk[db]);
+        element(1, 8 * m + 2 * db + 1, p1, ds1);
+        if (m == 1) tr_one(1, 0, db);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    seg_fix(1, p1, ds1);
+    pack(1, p1, ds1);
+    __builtin_amdgcn_sched_barrier(0);
+    // P4: block 1 gradients; its m = 1 transposed reads in the shadow of m = 0.
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      dv[db] = mfma_bf16(pf[1][0], dot[1][0][db], dv[db]);
+      tr_one(1, 1, db);
+      __builtin_amdgcn_sched_barrier(0);
+      dk[db] = mfma_bf16(sf[1][0], qtf[1][0][db], dk[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    grad_mfmas(1, 1);
+#else
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      read_ops(qb);
+      score_mfmas(qb);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      softmax(qb);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        read_tr(qb, m);
+        grad_mfmas(qb, m);
+      }
+    }
+#endif
   };
 
   // One step: wait for tile `it` (copies issued two steps ago), publish it to the

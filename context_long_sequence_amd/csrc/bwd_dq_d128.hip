@@ -2,14 +2,10 @@
 //   dQ_i += scale * sum_j P_ij (dP_ij - delta_i) k_j,  P recomputed from the final
 // log-sum-exp (archcrux, "sequence-parallel long-context attention OOM").
 // 4 waves x 32 queries of one query head walk the key tiles of the chunk; K and
-// V tiles are copied global -> LDS (swizzled, row-major) two steps ahead into a
-// ring of three slots, and the K^T operands of dQ^T += K^T dS^T come from
-// transposing reads of the same K tile.
+// V tiles are copied global -> LDS (swizzled, row-major; raw buffer loads, no
+// staging registers) two steps ahead into a ring of three slots, and the K^T
+// operands of dQ^T += K^T dS^T come from transposing reads of the same K tile.
 #include "bwd_d128.h"
-
-#ifndef RA_DQ_BATCH
-#define RA_DQ_BATCH 0  // 1: issue each MFMA chain's operand reads before its first MFMA (costs the second wave per SIMD)
-#endif
 
 namespace ra {
 namespace {
@@ -33,7 +29,8 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 vs1[kTile * kD];
   __shared__ __attribute__((aligned(1024))) __bf16 vs2[kTile * kD];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
   const int group = a.Hq / a.Hkv;
   int rem = logical;
@@ -54,9 +51,10 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
   const bool q_valid = qi < a.Sq;
   const int64_t qg = a.q_offset + qi;
 
-  const int64_t q_rs = (int64_t)a.Hq * kD, kv_rs = (int64_t)a.Hkv * kD;
-  const __bf16* kbase = static_cast<const __bf16*>(a.k) + (int64_t)b * a.Sk * kv_rs + (int64_t)g * kD;
-  const __bf16* vbase = static_cast<const __bf16*>(a.v) + (int64_t)b * a.Sk * kv_rs + (int64_t)g * kD;
+  const int64_t q_rs = (int64_t)a.Hq * kD;
+  const int kv_rb = a.Hkv * kD * 2;  // bytes between consecutive keys
+  const char* kbase = static_cast<const char*>(a.k) + ((int64_t)b * a.Sk * a.Hkv + g) * (kD * 2);
+  const char* vbase = static_cast<const char*>(a.v) + ((int64_t)b * a.Sk * a.Hkv + g) * (kD * 2);
 
   int n_keys = a.Sk;
   if (a.causal) {
@@ -95,17 +93,61 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
   const float neg_lse2 = lse_q == -INFINITY ? -INFINITY : -lse_q * kLog2e;
   const float dl = q_valid ? a.delta[li] : 0.0f;
 
+  // Visibility of key k0 + 16*half + i: i <= lim_base - k0 (causal rule, clamped to
+  // +-2^30 so that 32-bit arithmetic is exact; rows past Sq see nothing) and
+  // i <= Sk - 1 - k0 - 16*half (chunk end).
+  int lim_base = 1 << 30;
+  if (!q_valid)
+    lim_base = -(1 << 30);
+  else if (a.causal)
+    lim_base = (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, qg - a.kv_offset - 16 * half));
+
   f32x16 dq[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
 
-  // Copies key tile t (K and V, 32 rows each) global -> LDS without registers:
-  // two 16-byte copies per wave and tensor.
+  // Copies: 32 rows x 256 bytes per tile and tensor = 8 blocks of 1 KiB, two per
+  // wave; lane l of a block writes 16 bytes at 16*l, so it fetches the global chunk
+  // that the swizzle puts there.  Raw buffer loads with a per-tile descriptor whose
+  // range ends at the chunk's last key: rows past it read as zeros (and are masked).
+  uint32_t coff[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = (2 * wave + r) * 4 + (lane >> 4);
+    coff[r] = (uint32_t)(row * kv_rb + ((lane & 15) ^ swz(row)) * 16);
+  }
   auto issue = [&](int t, __bf16* kdst, __bf16* vdst) {
-    load_rows_lds<kTile, kDqWaves>(kdst, kbase + (int64_t)t * kTile * kv_rs, kv_rs, a.Sk - t * kTile, wave, lane);
-    load_rows_lds<kTile, kDqWaves>(vdst, vbase + (int64_t)t * kTile * kv_rs, kv_rs, a.Sk - t * kTile, wave, lane);
+    const int k0 = t * kTile;
+    const int64_t bytes = (int64_t)(a.Sk - 1 - k0) * kv_rb + kD * 2;
+    const buffer_rsrc rk = make_rsrc(kbase + (int64_t)k0 * kv_rb, bytes);
+    const buffer_rsrc rv = make_rsrc(vbase + (int64_t)k0 * kv_rb, bytes);
+    char* dk = reinterpret_cast<char*>(kdst) + 2 * wave * 1024;
+    char* dv = reinterpret_cast<char*>(vdst) + 2 * wave * 1024;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) buffer_load_lds16(rk, dk + r * 1024, coff[r]);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) buffer_load_lds16(rv, dv + r * 1024, coff[r]);
   };
-  constexpr int kCopiesPerTile = 2 * (kTile / 4 / kDqWaves);
+  constexpr int kCopiesPerTile = 4;  // per wave: K and V, two blocks each
+
+  // LDS operand offsets.  K and V rows (A of S^T = K Q^T, dP^T = V dO^T): row
+  // key_of_row(col), 16-byte chunk 2s+half, i.e. kA ^ (s << 5).  K^T (A of
+  // dQ^T += K^T dS^T) by transposing reads of rows 16*half + 8m + k (+4): two
+  // per-lane bases, the rest immediate.
+  const int krow = key_of_row(col);
+  const int kA = krow * 256 + 32 * (krow & 7) + 16 * (half ^ ((krow >> 4) & 1));
+  int t_even, t_odd;
+  {
+    const int s16 = lane & 15, mm = s16 & 3, kk = s16 >> 2;
+    const int x = (2 * ((lane >> 4) & 1) + (mm >> 1)) ^ (2 * kk + half);
+    const int base = 4096 * half + 256 * kk + 16 * (x & 3) + 8 * (mm & 1);
+    t_even = base + 64 * (x >> 2);
+    t_odd = base - 64 * (x >> 2);
+  }
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  auto tr_read = [](const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
+  };
 
   auto compute = [&](int t, const __bf16* kt_, const __bf16* vt_) {
       const int k0 = t * kTile;
@@ -118,19 +160,17 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
         const int sk_hi = seg_row[a.kv_offset + min(k0 + kTile, a.Sk) - 1];
         partial |= !(sk_lo == sk_hi && sk_lo == seg_w_lo && seg_w_lo == seg_w_hi);
       }
+      const char* kb = reinterpret_cast<const char*>(kt_);
+      const char* vb = reinterpret_cast<const char*>(vt_);
 
       // S^T = K Q^T and dP^T = V dO^T; register i of half h = key k0 + 16h + i.
       f32x16 st = f32x16{}, dpt = f32x16{};
       {
-        // Issue all 16 operand reads before the first MFMA, then interleave the two
-        // independent chains (keeps the LDS latency off the MFMA issue path).
-        const int row = key_of_row(col);
         bf16x8 fk[8], fv[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) fk[s] = read_chunk(kt_, row, 2 * s + half);
+        for (int s = 0; s < 8; ++s) fk[s] = load_bf16x8(kb + (kA ^ (s << 5)));
 #pragma unroll
-        for (int s = 0; s < 8; ++s) fv[s] = read_chunk(vt_, row, 2 * s + half);
-        if constexpr (RA_DQ_BATCH) __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < 8; ++s) fv[s] = load_bf16x8(vb + (kA ^ (s << 5)));
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           st = mfma_bf16(fk[s], qf[s], st);
@@ -141,13 +181,19 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(st[i], a.scale_log2, neg_lse2));
       if (partial) {  // one wave-uniform branch around the element mask
+        const int lim = min(lim_base - k0, a.Sk - 1 - k0 - 16 * half);
+        if constexpr (kSeg) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kj = k0 + 16 * half + i;
-          bool vis = q_valid && kj < a.Sk;
-          if (a.causal) vis = vis && (a.kv_offset + kj <= qg);
-          if constexpr (kSeg) vis = vis && (kj < a.Sk ? seg_row[a.kv_offset + kj] == seg_q : false);
-          p[i] = vis ? p[i] : 0.0f;
+          for (int i = 0; i < 16; ++i) {
+            // Wave-uniform addresses (scalar loads), clamped into the chunk.
+            const int s_lo = seg_row[a.kv_offset + min(k0 + i, a.Sk - 1)];
+            const int s_hi = seg_row[a.kv_offset + min(k0 + 16 + i, a.Sk - 1)];
+            const bool vis = (i <= lim) & ((half ? s_hi : s_lo) == seg_q);
+            p[i] = vis ? p[i] : 0.0f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) p[i] = (i <= lim) ? p[i] : 0.0f;
         }
       }
 #pragma unroll
@@ -159,8 +205,12 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
                                     ds[8 * m + 5], ds[8 * m + 6], ds[8 * m + 7]);
         bf16x8 kt[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) kt[db] = read_transposed(kt_, 16 * half + 8 * m, 32 * db, lane);
-        if constexpr (RA_DQ_BATCH) __builtin_amdgcn_sched_barrier(0);
+        for (int db = 0; db < 4; ++db) {
+          const char* p0 = kb + ((db & 1) ? t_odd : t_even) + 64 * db + 2048 * m;
+          const bf16x4_t x0 = tr_read(p0);
+          const bf16x4_t x1 = tr_read(p0 + 1024 + (db < 2 ? 128 : -128));
+          kt[db] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        }
 #pragma unroll
         for (int db = 0; db < 4; ++db) dq[db] = mfma_bf16(kt[db], sf, dq[db]);
       }
@@ -182,12 +232,14 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
     compute(t, kc, vc);
   };
 
-  if (kt_begin < kt_end) issue(kt_begin, ks0, vs0);
-  if (kt_begin + 1 < kt_end) issue(kt_begin + 1, ks1, vs1);
-  for (int t = kt_begin; t < kt_end; t += 3) {
-    step(t, ks0, vs0, ks2, vs2);
-    if (t + 1 < kt_end) step(t + 1, ks1, vs1, ks0, vs0);
-    if (t + 2 < kt_end) step(t + 2, ks2, vs2, ks1, vs1);
+  if (kt_begin < kt_end) {
+    issue(kt_begin, ks0, vs0);
+    if (kt_begin + 1 < kt_end) issue(kt_begin + 1, ks1, vs1);
+    for (int t = kt_begin; t < kt_end; t += 3) {
+      step(t, ks0, vs0, ks2, vs2);
+      if (t + 1 < kt_end) step(t + 1, ks1, vs1, ks0, vs0);
+      if (t + 2 < kt_end) step(t + 2, ks2, vs2, ks1, vs1);
+    }
   }
 
   if (q_valid) {

@@ -386,7 +386,8 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
   __shared__ __attribute__((aligned(1024))) __bf16 vs1[BN * D];
   __shared__ __attribute__((aligned(1024))) __bf16 vs2[BN * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
   const int group = a.Hq / a.Hkv;
   int rem = logical;
