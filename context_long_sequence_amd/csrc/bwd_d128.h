@@ -4,9 +4,6 @@
 #include "ra_device.h"
 #include "ra_host.h"
 
-#ifndef RA_DKDV_QBLOCKS
-#define RA_DKDV_QBLOCKS 2  // 32-query blocks per staged query tile of the bf16 d=128 dK/dV kernel
-#endif
 #ifndef RA_DKDV_WAVES
 #define RA_DKDV_WAVES 4  // waves (x 32 keys) per dK/dV workgroup of the bf16 d=128 path
 #endif
@@ -59,31 +56,7 @@ __device__ __forceinline__ void seg_tile_range(const int32_t* row, int n, int ti
 }
 
 constexpr int kD128 = 128;
-constexpr int kD128Tile = 32;  // rows per staged tile (keys for dQ, queries for dK/dV)
-
-// Register prefetch of one ROWS-row x 128-column bf16 tile by NT threads.
-template <int NT, int ROWS = 32>
-struct TileStage {
-  static constexpr int kPer = ROWS * 16 / NT;  // 16-byte chunks per thread
-  static_assert(kPer * NT == ROWS * 16, "tile must split evenly over the threads");
-  u32x4 reg[kPer];
-  // rows [row0, row0 + ROWS) of a [rows, stride] matrix, rows clamped to nrows-1
-  __device__ __forceinline__ void fetch(const __bf16* base, int64_t stride, int row0, int nrows, int tid) {
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int u = tid + r * NT;
-      const int row = min(row0 + (u >> 4), nrows - 1);
-      reg[r] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * stride + (u & 15) * 8);
-    }
-  }
-  __device__ __forceinline__ void put(__bf16* tile, int tid) const {
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      const int u = tid + r * NT;
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(tile) + tile_off(u >> 4, u & 15)) = reg[r];
-    }
-  }
-};
+constexpr int kD128Tile = 32;  // keys per staged tile of the dQ kernel
 
 // bf16, head_dim 128: dK/dV kernel (bwd_dkdv_d128.hip) then dQ kernel
 // (bwd_dq_d128.hip) on `stream`.

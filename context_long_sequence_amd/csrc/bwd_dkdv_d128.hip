@@ -6,18 +6,14 @@
 // and walks the 64-query tiles of every query head of the group.  Q and dO tiles
 // are copied global -> LDS (swizzled, row-major; raw buffer loads, no staging
 // registers) two steps ahead into a ring of three slots; their transposes are
-// read with transposing LDS reads.
+// read with transposing LDS reads.  The tile body is a hand-placed MFMA / vector
+// ALU pipeline (see compute below).
 #include "bwd_d128.h"
-
-#ifndef RA_DKDV_SCHED
-#define RA_DKDV_SCHED 0
-#endif
 
 namespace ra {
 namespace {
 
 constexpr int kD = kD128;
-constexpr int kTile = kD128Tile;
 
 // ------------------------------------------------------------------------------------
 // dK, dV: NW waves x 32 keys of one KV head; walks the 32-query tiles of every
@@ -152,17 +148,11 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   // LDS operand offsets.  Q and dO rows (A of S = Q K^T, dP = dO V^T): row
   // 32*qb + key_of_row(col), 16-byte chunk 2c+half, i.e. 8192*qb + (rA ^ (c << 5)).
   // dO^T and Q^T (B of dV += P^T dO, dK += dS^T Q) by transposing reads of rows
-  // 32*qb + 16*half + 8m + k (+4): two per-lane bases, the rest immediate.
-  const int rrow = key_of_row(col);
-  const int rA = rrow * 256 + 32 * (rrow & 7) + 16 * (half ^ ((rrow >> 4) & 1));
-  int t_even, t_odd;
-  {
-    const int s16 = lane & 15, mm = s16 & 3, kk = s16 >> 2;
-    const int x = (2 * ((lane >> 4) & 1) + (mm >> 1)) ^ (2 * kk + half);
-    const int base = 4096 * half + 256 * kk + 16 * (x & 3) + 8 * (mm & 1);
-    t_even = base + 64 * (x >> 2);
-    t_odd = base - 64 * (x >> 2);
-  }
+  // 32*qb + 16*half + 8m + k (+4): per-lane bases B0 (rows +k) and B1 (rows +4+k);
+  // column block db selects bits 6-7 by XOR, m and qb add 2048 and 8192 bytes.
+  const int rA = row_read_base(lane);
+  const TrBases trb = tr_bases(lane);
+  const int tB0 = trb.b0, tB1 = trb.b1;
   typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
   auto tr_read = [](const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
@@ -175,274 +165,160 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   // LSE is -inf sees no key at all, so its elements are masked in every block that
   // holds it.  The bounds mask is applied to every block (it also zeroes blocks
   // that lie entirely before the wave's keys); the segment test only where needed.
+  // One 64-query tile = two 32-query blocks against the wave's 32 keys.  Per block:
+  // score MFMAs (S = Q K^T, dP = dO V^T; lane = key, register i of half h = query
+  // q0 + 16h + i), per element P = exp(S - LSE) and dS = P (dP - delta) on the
+  // vector ALU, then gradient MFMAs (dV += P^T dO, dK += dS^T Q).  With one wave per
+  // SIMD the two units only work side by side if the instruction stream interleaves
+  // them, so the tile is laid out as a pipeline pinned with scheduling fences:
+  //   P1: block 0 scores                  | block 1 operand reads
+  //   P2: block 1 scores                  | block 0 elements, block 0 dO^T/Q^T reads
+  //   P3: block 0 gradients               | block 1 elements, block 1 dO^T/Q^T reads
+  //   P4: block 1 gradients
+  // Each MFMA slot (32 clocks) carries at most one element.  P uses the final LSE as
+  // is: a query whose LSE is -inf sees no key at all, so the element mask zeroes it.
   auto compute = [&](int it, const __bf16* qt_, const __bf16* dt_, const float* xs) {
     const int qtile0 = (qt_begin + it % n_q) * QT;
     const char* qc = reinterpret_cast<const char*>(qt_);
     const char* dc = reinterpret_cast<const char*>(dt_);
-    // S = Q K^T and dP = dO V^T: lane = key, register i of half h = query q0 + 16h + i.
     f32x16 s[2], dp[2];
-    bf16x8 fq[2][8], fd[2][8];
-    auto read_ops = [&](int qb) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        fq[qb][c] = load_bf16x8(qc + 8192 * qb + (rA ^ (c << 5)));
-        fd[qb][c] = load_bf16x8(dc + 8192 * qb + (rA ^ (c << 5)));
-      }
+    bf16x8 fq[2][8], fd[2][8];            // A operands of the score MFMAs
+    bf16x8 dot[2][2][4], qtf[2][2][4];    // [qb][m][db]: dO^T and Q^T operands
+    bf16x8 pf[2][2], sf[2][2];            // [qb][m]: packed P and dS, elements 8m..8m+7
+    float lq[2][16], dl[2][16];           // -LSE*log2(e) and delta of the block's queries
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    auto read_op = [&](int qb, int c) {
+      fq[qb][c] = load_bf16x8(qc + 8192 * qb + (rA ^ (c << 5)));
+      fd[qb][c] = load_bf16x8(dc + 8192 * qb + (rA ^ (c << 5)));
     };
-    auto score_mfmas = [&](int qb) {
-      s[qb] = f32x16{};
-      dp[qb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        s[qb] = mfma_bf16(fq[qb][c], kf[c], s[qb]);
-        dp[qb] = mfma_bf16(fd[qb][c], vf[c], dp[qb]);
-      }
-    };
-    // Softmax-side vector work of block qb: P and dS as bf16 MFMA operands.
-    bf16x8 pf[2][2], sf[2][2];
-    auto softmax = [&](int qb) {
-      const int q0 = qtile0 + 32 * qb;
-      const float* lse_q = xs + 32 * qb + 16 * half;
-      const float* del_q = xs + QT + 32 * qb + 16 * half;
-      float p[16], dsv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(s[qb][i], a.scale_log2, lse_q[i] * -kLog2e));
-      {
-        const int lo = vis_lo - q0, hi = vis_hi - q0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = ((i >= lo) & (i < hi)) ? p[i] : 0.0f;
-      }
-      if constexpr (kSeg) {
-        // Segment ids are nondecreasing: only blocks that straddle a segment
-        // boundary need the per-element segment test.
-        const int sq_lo = __builtin_bit_cast(int, xs[2 * QT + 32 * qb]);
-        const int sq_hi = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 31]);
-        if (!(sq_lo == sq_hi && sq_lo == seg_w_lo && seg_w_lo == seg_w_hi)) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            p[i] = (__builtin_bit_cast(int, xs[2 * QT + 32 * qb + 16 * half + i]) == seg_k) ? p[i] : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dsv[i] = p[i] * (dp[qb][i] - del_q[i]);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        pf[qb][m] = to_bf16x8(p[8 * m], p[8 * m + 1], p[8 * m + 2], p[8 * m + 3], p[8 * m + 4], p[8 * m + 5],
-                              p[8 * m + 6], p[8 * m + 7]);
-        sf[qb][m] = to_bf16x8(dsv[8 * m], dsv[8 * m + 1], dsv[8 * m + 2], dsv[8 * m + 3], dsv[8 * m + 4],
-                              dsv[8 * m + 5], dsv[8 * m + 6], dsv[8 * m + 7]);
-      }
-    };
-    // dO^T and Q^T operands of block qb (transposing reads), then dV += P^T dO, dK += dS^T Q.
-    bf16x8 dot[2][2][4], qtf[2][2][4];
-    auto read_tr = [&](int qb, int m) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int o = ((db & 1) ? t_odd : t_even) + 64 * db + 2048 * m + 8192 * qb;
-        const int o1 = o + 1024 + (db < 2 ? 128 : -128);
-        const bf16x4_t d0 = tr_read(dc + o), d1 = tr_read(dc + o1);
-        const bf16x4_t q0v = tr_read(qc + o), q1v = tr_read(qc + o1);
-        dot[qb][m][db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-        qtf[qb][m][db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
-      }
-    };
-    auto grad_mfmas = [&](int qb, int m) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        dv[db] = mfma_bf16(pf[qb][m], dot[qb][m][db], dv[db]);
-        dk[db] = mfma_bf16(sf[qb][m], qtf[qb][m][db], dk[db]);
-      }
-    };
-#if RA_DKDV_SCHED == 1
-    // Each MFMA chain's operand reads issued as a batch before its first MFMA.
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      read_ops(qb);
-      __builtin_amdgcn_sched_barrier(0);
-      score_mfmas(qb);
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      softmax(qb);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        read_tr(qb, m);
-        __builtin_amdgcn_sched_barrier(0);
-        grad_mfmas(qb, m);
-      }
-    }
-#elif RA_DKDV_SCHED == 2
-    // Explicit pipeline: block 1's operand reads under block 0's score MFMAs; block
-    // 0's softmax and transposed reads under block 1's score MFMAs; block 1's
-    // softmax and transposed reads under block 0's gradient MFMAs.
-    read_ops(0);
-    __builtin_amdgcn_sched_barrier(0);
-    score_mfmas(0);
-    read_ops(1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    score_mfmas(1);
-    softmax(0);
-    read_tr(0, 0);
-    read_tr(0, 1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // VALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    grad_mfmas(0, 0);
-    grad_mfmas(0, 1);
-    softmax(1);
-    read_tr(1, 0);
-    read_tr(1, 1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 2);  // VALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    grad_mfmas(1, 0);
-    grad_mfmas(1, 1);
-#elif RA_DKDV_SCHED == 3
-    // Hand-placed pipeline, pinned with scheduling fences: each MFMA slot (32 clocks)
-    // carries one element of the other block's softmax and a few LDS reads, so one
-    // wave keeps the matrix core busy while its vector ALU works.
-    float lq[2][16], dq_[2][16];
     auto read_rows = [&](int qb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         lq[qb][i] = xs[32 * qb + 16 * half + i] * -kLog2e;
-        dq_[qb][i] = xs[QT + 32 * qb + 16 * half + i];
+        dl[qb][i] = xs[QT + 32 * qb + 16 * half + i];
       }
     };
-    float p0[16], ds0[16];
-    auto element = [&](int qb, int i, float* pp, float* dd) {
-      const int q0 = qtile0 + 32 * qb;
-      float pv = exp2_fast(__builtin_fmaf(s[qb][i], a.scale_log2, lq[qb][i]));
-      pv = ((i >= vis_lo - q0) & (i < vis_hi - q0)) ? pv : 0.0f;
-      float dv_ = pv * (dp[qb][i] - dq_[qb][i]);
-      // Pin the element to its slot: the empty statement is ordered with the
-      // scheduling fences, so the arithmetic cannot sink towards its later use.
-      asm volatile("" : "+v"(pv), "+v"(dv_));
-      pp[i] = pv;
-      dd[i] = dv_;
+    auto read_tr = [&](int qb, int m, int db) {
+      const int o = (tB0 ^ (db << 6)) + 2048 * m + 8192 * qb;
+      const int o1 = (tB1 ^ (db << 6)) + 2048 * m + 8192 * qb;
+      const bf16x4_t d0 = tr_read(dc + o), d1 = tr_read(dc + o1);
+      const bf16x4_t q0v = tr_read(qc + o), q1v = tr_read(qc + o1);
+      dot[qb][m][db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      qtf[qb][m][db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
     };
-    auto seg_fix = [&](int qb, float* pp, float* dd) {
+    float pe[2][16], de[2][16];
+    auto element = [&](int qb, int i) {
+      float pv = exp2_fast(__builtin_fmaf(s[qb][i], a.scale_log2, lq[qb][i]));
+      float dv_ = pv * (dp[qb][i] - dl[qb][i]);
+      // The empty statement is ordered with the fences, so the element cannot sink
+      // towards its later use.
+      asm volatile("" : "+v"(pv), "+v"(dv_));
+      pe[qb][i] = pv;
+      de[qb][i] = dv_;
+    };
+    // Element mask, applied after a block's elements and only where the block is not
+    // entirely visible (wave-uniform test): the causal rule, the ends of the query
+    // shard and of the chunk, and (packed rows) the segment test.  Selects, so an
+    // infinite P of an invisible element never reaches dV or dK.
+    auto mask_and_pack = [&](int qb) {
+      const int q0 = qtile0 + 32 * qb;
+      bool partial = (q0 + 32 > a.Sq) || (kw + 32 > a.Sk);
+      if (a.causal) partial |= (a.kv_offset + kw + 31 > a.q_offset + q0);
+      if (partial) {
+        const int lo = vis_lo - q0, hi = vis_hi - q0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool vis = (i >= lo) & (i < hi);
+          pe[qb][i] = vis ? pe[qb][i] : 0.0f;
+          de[qb][i] = vis ? de[qb][i] : 0.0f;
+        }
+      }
       if constexpr (kSeg) {
+        // Segment ids are nondecreasing: only blocks that straddle a segment boundary
+        // need the per-element segment test.
         const int sq_lo = __builtin_bit_cast(int, xs[2 * QT + 32 * qb]);
         const int sq_hi = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 31]);
         if (!(sq_lo == sq_hi && sq_lo == seg_w_lo && seg_w_lo == seg_w_hi)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const bool ok = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 16 * half + i]) == seg_k;
-            pp[i] = ok ? pp[i] : 0.0f;
-            dd[i] = ok ? dd[i] : 0.0f;
+            pe[qb][i] = ok ? pe[qb][i] : 0.0f;
+            de[qb][i] = ok ? de[qb][i] : 0.0f;
           }
         }
       }
-    };
-    auto pack = [&](int qb, const float* pp, const float* dd) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        pf[qb][m] = to_bf16x8(pp[8 * m], pp[8 * m + 1], pp[8 * m + 2], pp[8 * m + 3], pp[8 * m + 4], pp[8 * m + 5],
-                              pp[8 * m + 6], pp[8 * m + 7]);
-        sf[qb][m] = to_bf16x8(dd[8 * m], dd[8 * m + 1], dd[8 * m + 2], dd[8 * m + 3], dd[8 * m + 4],
-                              dd[8 * m + 5], dd[8 * m + 6], dd[8 * m + 7]);
+        const float* pp = &pe[qb][8 * m];
+        const float* dd = &de[qb][8 * m];
+        pf[qb][m] = to_bf16x8(pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]);
+        sf[qb][m] = to_bf16x8(dd[0], dd[1], dd[2], dd[3], dd[4], dd[5], dd[6], dd[7]);
       }
     };
-    auto tr_one = [&](int qb, int m, int db) {
-      const int o = ((db & 1) ? t_odd : t_even) + 64 * db + 2048 * m + 8192 * qb;
-      const int o1 = o + 1024 + (db < 2 ? 128 : -128);
-      const bf16x4_t d0 = tr_read(dc + o), d1 = tr_read(dc + o1);
-      const bf16x4_t q0v = tr_read(qc + o), q1v = tr_read(qc + o1);
-      dot[qb][m][db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-      qtf[qb][m][db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
-    };
-    // P0: block 0 operands and row scalars.
-    read_ops(0);
-    read_rows(0);
-    __builtin_amdgcn_sched_barrier(0);
+
     // P1: block 0 scores; block 1 operand reads in their shadow.
+#pragma unroll
+    for (int c = 0; c < 8; ++c) read_op(0, c);
+    read_rows(0);
+    fence();
     s[0] = f32x16{};
     dp[0] = f32x16{};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       s[0] = mfma_bf16(fq[0][c], kf[c], s[0]);
       fq[1][c] = load_bf16x8(qc + 8192 + (rA ^ (c << 5)));
-      __builtin_amdgcn_sched_barrier(0);
+      fence();
       dp[0] = mfma_bf16(fd[0][c], vf[c], dp[0]);
       fd[1][c] = load_bf16x8(dc + 8192 + (rA ^ (c << 5)));
-      __builtin_amdgcn_sched_barrier(0);
+      fence();
     }
     read_rows(1);
-    __builtin_amdgcn_sched_barrier(0);
-    // P2: block 1 scores; block 0 softmax and block 0 transposed reads (m = 0).
+    fence();
+    // P2: block 1 scores; block 0 elements and its m = 0 transposed reads.
     s[1] = f32x16{};
     dp[1] = f32x16{};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       s[1] = mfma_bf16(fq[1][c], kf[c], s[1]);
-      element(0, 2 * c, p0, ds0);
-      if (c < 4) tr_one(0, 0, c);
-      __builtin_amdgcn_sched_barrier(0);
+      element(0, 2 * c);
+      if (c < 4) read_tr(0, 0, c);
+      fence();
       dp[1] = mfma_bf16(fd[1][c], vf[c], dp[1]);
-      element(0, 2 * c + 1, p0, ds0);
-      __builtin_amdgcn_sched_barrier(0);
+      element(0, 2 * c + 1);
+      fence();
     }
-    seg_fix(0, p0, ds0);
-    pack(0, p0, ds0);
-    __builtin_amdgcn_sched_barrier(0);
-    // P3: block 0 gradients; block 1 softmax and the remaining transposed reads.
-    float p1[16], ds1[16];
+    mask_and_pack(0);
+    fence();
+    // P3: block 0 gradients; block 1 elements and the remaining transposed reads.
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         dv[db] = mfma_bf16(pf[0][m], dot[0][m][db], dv[db]);
-        element(1, 8 * m + 2 * db, p1, ds1);
-        if (m == 0) tr_one(0, 1, db);
-        __builtin_amdgcn_sched_barrier(0);
+        element(1, 8 * m + 2 * db);
+        if (m == 0) read_tr(0, 1, db);
+        fence();
         dk[db] = mfma_bf16(sf[0][m], qtf[0][m][db], dk[db]);
-        element(1, 8 * m + 2 * db + 1, p1, ds1);
-        if (m == 1) tr_one(1, 0, db);
-        __builtin_amdgcn_sched_barrier(0);
+        element(1, 8 * m + 2 * db + 1);
+        if (m == 1) read_tr(1, 0, db);
+        fence();
       }
-    seg_fix(1, p1, ds1);
-    pack(1, p1, ds1);
-    __builtin_amdgcn_sched_barrier(0);
+    mask_and_pack(1);
+    fence();
     // P4: block 1 gradients; its m = 1 transposed reads in the shadow of m = 0.
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       dv[db] = mfma_bf16(pf[1][0], dot[1][0][db], dv[db]);
-      tr_one(1, 1, db);
-      __builtin_amdgcn_sched_barrier(0);
+      read_tr(1, 1, db);
+      fence();
       dk[db] = mfma_bf16(sf[1][0], qtf[1][0][db], dk[db]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    grad_mfmas(1, 1);
-#else
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      read_ops(qb);
-      score_mfmas(qb);
+      fence();
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      softmax(qb);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        read_tr(qb, m);
-        grad_mfmas(qb, m);
-      }
+    for (int db = 0; db < 4; ++db) {
+      dv[db] = mfma_bf16(pf[1][1], dot[1][1][db], dv[db]);
+      dk[db] = mfma_bf16(sf[1][1], qtf[1][1][db], dk[db]);
     }
-#endif
   };
 
   // One step: wait for tile `it` (copies issued two steps ago), publish it to the

@@ -132,18 +132,12 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
 
   // LDS operand offsets.  K and V rows (A of S^T = K Q^T, dP^T = V dO^T): row
   // key_of_row(col), 16-byte chunk 2s+half, i.e. kA ^ (s << 5).  K^T (A of
-  // dQ^T += K^T dS^T) by transposing reads of rows 16*half + 8m + k (+4): two
-  // per-lane bases, the rest immediate.
-  const int krow = key_of_row(col);
-  const int kA = krow * 256 + 32 * (krow & 7) + 16 * (half ^ ((krow >> 4) & 1));
-  int t_even, t_odd;
-  {
-    const int s16 = lane & 15, mm = s16 & 3, kk = s16 >> 2;
-    const int x = (2 * ((lane >> 4) & 1) + (mm >> 1)) ^ (2 * kk + half);
-    const int base = 4096 * half + 256 * kk + 16 * (x & 3) + 8 * (mm & 1);
-    t_even = base + 64 * (x >> 2);
-    t_odd = base - 64 * (x >> 2);
-  }
+  // dQ^T += K^T dS^T) by transposing reads of rows 16*half + 8m + k (+4): per-lane
+  // bases B0 (rows +k) and B1 (rows +4+k); column block db selects bits 6-7 by XOR,
+  // m adds 2048 bytes.
+  const int kA = row_read_base(lane);
+  const TrBases trb = tr_bases(lane);
+  const int tB0 = trb.b0, tB1 = trb.b1;
   typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
   auto tr_read = [](const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
@@ -206,9 +200,8 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
         bf16x8 kt[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const char* p0 = kb + ((db & 1) ? t_odd : t_even) + 64 * db + 2048 * m;
-          const bf16x4_t x0 = tr_read(p0);
-          const bf16x4_t x1 = tr_read(p0 + 1024 + (db < 2 ? 128 : -128));
+          const bf16x4_t x0 = tr_read(kb + (tB0 ^ (db << 6)) + 2048 * m);
+          const bf16x4_t x1 = tr_read(kb + (tB1 ^ (db << 6)) + 2048 * m);
           kt[db] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         }
 #pragma unroll

@@ -103,17 +103,45 @@ __device__ __forceinline__ int key_of_row(int r) { return 16 * ((r >> 2) & 1) + 
 
 // ---- LDS tiles of 128-element bf16 rows (256 B per row, no padding) ------------------
 // The 16 chunks of 16 bytes of row r are stored XOR-swizzled at chunk position
-// c ^ swz(r).  swz uses bits 0,1,2 and 4 of the row, which makes both operand read
-// patterns of the kernels conflict-free: 16 lanes reading one logical chunk of rows
-// {0-3, 16-19, 4-7, 20-23} (or the +8 set), and 16 lanes transposing 4 consecutive
-// rows x 32 bytes.  Rows are filled by direct global->LDS loads (lane l of a wave
-// writes bytes [16l, 16l+16) of a 1 KiB block = 4 rows), so the swizzle is applied
-// on the global side by choosing which chunk each lane fetches.
+// c ^ swz(r), swz(r) = 4*(r & 3) + 2*((r >> 2) & 1) + ((r >> 4) & 1).  Both operand
+// read patterns of the kernels are then conflict-free: 16 lanes reading one logical
+// chunk of rows {0-3, 16-19, 4-7, 20-23} (or the +8 set) with 16-byte reads, and 32
+// lanes of transposing 8-byte reads covering 4 consecutive rows x 64 bytes (the
+// (r & 3) << 2 term spreads those 4 rows over all 64 banks).  Rows are filled by
+// direct global->LDS loads (lane l of a wave writes bytes [16l, 16l+16) of a 1 KiB
+// block = 4 rows), so the swizzle is applied on the global side by choosing which
+// chunk each lane fetches.
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-__device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 4) & 1); }
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 4) & 1); }
 
 __device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
+
+// Byte offsets of the two MFMA operand reads of such tiles.
+//
+// Row reads (16 bytes): lane l reads chunk 2s + l/32 of row key_of_row(l % 32) (plus
+// a multiple of 32 rows); its offset is row_read_base(l) ^ (s << 5).
+__device__ __forceinline__ int row_read_base(int lane) {
+  const int r = key_of_row(lane & 31), h = lane >> 5;
+  return r * 256 + 32 * (2 * (r & 3) + ((r >> 2) & 1)) + 16 * (h ^ ((r >> 4) & 1));
+}
+// Transposing reads (ds_read_b64_tr_b16): within a group of 16 lanes, lane j
+// receives element j % 4 of the 8-byte words addressed by lanes j/4 + 4k (k = 0..3).
+// Addressing row r0 + k at columns c0 + 4m .. +3 from lane m + 4k therefore hands
+// lane j rows r0 .. r0+3 of column c0 + j.  Two reads (rows +0..3, +4..7) give lane l
+// the 8 bf16 of one MFMA operand: column 32*db + l % 32 of rows 16*(l/32) + 8m ..
+// +7 (plus a multiple of 32 rows).  With the swizzle above their offsets are
+// (b0 ^ (db << 6)) + 2048*m and (b1 ^ (db << 6)) + 2048*m.
+struct TrBases {
+  int b0, b1;
+};
+__device__ __forceinline__ TrBases tr_bases(int lane) {
+  const int s16 = lane & 15, mm = s16 & 3, kk = s16 >> 2, h = lane >> 5;
+  const int x = 2 * ((lane >> 4) & 1) + (mm >> 1);
+  const int sub8 = 8 * (mm & 1);
+  return TrBases{(16 * h + kk) * 256 + 64 * kk + 16 * (x ^ h) + sub8,
+                 (16 * h + 4 + kk) * 256 + 64 * kk + 16 * (x ^ (2 + h)) + sub8};
+}
 
 // Combines the two half-waves: lane l and lane l^32 both get op(x[l mod 32],
 // x[32 + l mod 32]) (v_permlane32_swap: one VALU op, no LDS round trip).
@@ -140,54 +168,6 @@ __device__ __forceinline__ void buffer_load_lds4(buffer_rsrc rs, void* dst, uint
 // 16 bytes per lane from base + voffset into LDS at dst + 16*lane (dst wave-uniform).
 __device__ __forceinline__ void buffer_load_lds16(buffer_rsrc rs, void* dst, uint32_t voffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, voffset, 0, 0, 0);
-}
-
-// Wait until every global->LDS load issued by this wave has landed.
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Copies `rows` rows of 128 bf16 (row r from src + r*row_stride, clamped to
-// valid_rows-1 so every fetch stays in bounds) into a swizzled LDS tile.  The
-// tile's 1 KiB blocks are spread over the workgroup's `waves` waves.
-template <int ROWS, int WAVES>
-__device__ __forceinline__ void load_rows_lds(__bf16* tile, const __bf16* src, int64_t row_stride, int valid_rows,
-                                              int wave, int lane) {
-  static_assert(ROWS % (4 * WAVES) == 0, "rows per wave must be a multiple of 4");
-  constexpr int kBlocks = ROWS / 4 / WAVES;
-#pragma unroll
-  for (int r = 0; r < kBlocks; ++r) {
-    const int blk = wave * kBlocks + r;
-    const int row = blk * 4 + (lane >> 4);
-    const int chunk = (lane & 15) ^ swz(row);
-    const int grow = min(row, valid_rows - 1);
-    const __bf16* g = src + (int64_t)grow * row_stride + chunk * 8;
-    __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)(reinterpret_cast<char*>(tile) + blk * 1024), 16, 0, 0);
-  }
-}
-
-// 16-byte operand read: logical chunk `chunk` of row `row` of a swizzled tile.
-__device__ __forceinline__ bf16x8 read_chunk(const __bf16* tile, int row, int chunk) {
-  return load_bf16x8(reinterpret_cast<const char*>(tile) + tile_off(row, chunk));
-}
-
-// Transposing operand read (ds_read_b64_tr_b16) of a swizzled tile: lane l gets, as
-// 8 bf16, column col0 + (l % 32) of rows row8 .. row8+7 (row8 may differ between the
-// two half-waves).  Each call issues two transposing reads of 4 rows.  Within a
-// 16-lane group, source lane s = m + 4k addresses row (base + k) at columns
-// colbase + 4m .. +3; the hardware returns to lane j element (j % 4) of the
-// addresses of lanes j/4 + 4k, k = 0..3, i.e. rows base+0..3 of column colbase + j.
-__device__ __forceinline__ bf16x8 read_transposed(const __bf16* tile, int row8, int col0, int lane) {
-  const int s = lane & 15;
-  const int m = s & 3, k = s >> 2;
-  const int colbase = col0 + (lane & 16);           // 16-column half of the 32 columns
-  const int c = (colbase >> 3) + (m >> 1);          // logical 16-byte chunk
-  const int sub8 = (m & 1) * 8;                     // byte offset inside the chunk
-  typedef __bf16 v4 __attribute__((ext_vector_type(4)));
-  const char* base = reinterpret_cast<const char*>(tile);
-  const int r0 = row8 + k, r1 = row8 + 4 + k;
-  v4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4*)(base + tile_off(r0, c) + sub8));
-  v4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4*)(base + tile_off(r1, c) + sub8));
-  bf16x8 out = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-  return out;
 }
 
 // Workgroup -> XCD remap.  Consecutive workgroup ids are dispatched round-robin
