@@ -250,6 +250,12 @@ def main():
 
     if not args.no_extras:
         extra.update(side_measurements(torch, ra, np, dev, CONFIGS, make_workload))
+        zz = extra["zigzag_64k_cp8"]
+        # the ring runs at the pace of its slowest rank: contiguous rank 7 (this line's
+        # step) against the slower of zigzag ranks 0 and 7 (all ranks have equal work)
+        if args.only == "all":
+            zz["critical_path_speedup_vs_contiguous"] = round(
+                ms_per_step / max(zz["rank0"]["ms"], zz[f"rank{zz['cp'] - 1}"]["ms"]), 3)
 
     if args.profile_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -303,8 +309,9 @@ def packed_live_pairs(lengths, C, rank):
 
 
 def side_measurements(torch, ra, np, dev, CONFIGS, make_workload):
-    """Forward TFLOP/s of the 8K and packed-16K shares, the segment-id kernel time, and
-    the peak workspace of one forward+backward at S = 16K..128K (CP=8, rank 7)."""
+    """Forward TFLOP/s of the 8K and packed-16K shares, the segment-id kernel time, the
+    load-balanced (zigzag) 64K forward+backward of ranks 0 and 7, and the peak workspace
+    of one forward+backward at S = 16K..128K (CP=8, rank 7)."""
     out = {}
 
     def ev_ms(fn, reps=5):
@@ -353,6 +360,34 @@ def side_measurements(torch, ra, np, dev, CONFIGS, make_workload):
         "fwd_ms": round(fms, 4), "fwd_tflops": round(4.0 * c4.Hq * c4.d * pairs4 / (fms * 1e-3) / 1e12, 2),
         "bwd_ms": round(bms, 4), "bwd_tflops": round(10.0 * c4.Hq * c4.d * pairs4 / (bms * 1e-3) / 1e12, 2)}
     del q, ks, vs, do, ws, o4, l4
+
+    # load-balanced (zigzag) layout at the 64K shape: ranks 0 and 7, forward + backward
+    S, cp, Hq, Hkv, d = 65536, 8, 32, 8, 128
+    h = S // (2 * cp)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    zq = torch.randn((1, 2 * h, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    zk = [torch.randn((1, 2 * h, Hkv, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(cp)]
+    zv = [torch.randn((1, 2 * h, Hkv, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(cp)]
+    zdo = torch.randn((1, 2 * h, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    zo = torch.empty_like(zq)
+    zl = torch.empty((2, Hq, h), dtype=torch.float32, device=dev)
+    zdq = torch.zeros((1, 2 * h, Hq, d), dtype=torch.float32, device=dev)
+    zdk = [torch.zeros((1, 2 * h, Hkv, d), dtype=torch.float32, device=dev) for _ in range(cp)]
+    zdv = [torch.zeros((1, 2 * h, Hkv, d), dtype=torch.float32, device=dev) for _ in range(cp)]
+    zws = ra.ZigzagWorkspace(h, Hq, d, dev, backward=True)
+    pairs_z = 2 * cp * h * h + h  # visible pairs of every rank in this layout
+    zz = {"seq_len": S, "cp": cp, "live_pairs_per_rank": pairs_z}
+    for r in (0, cp - 1):
+        def fb(r=r):
+            ra.ring_forward_zigzag(zq, zk, zv, r, cp, causal=True, out=zo, lse=zl, workspace=zws)
+            ra.ring_backward_zigzag(zq, zk, zv, zo, zl, zdo, r, cp, causal=True, dq=zdq, dk_ranks=zdk, dv_ranks=zdv,
+                                    workspace=zws)
+        ms = ev_ms(fb, reps=3)
+        zz[f"rank{r}"] = {"ms": round(ms, 3), "tflops": round(14.0 * Hq * d * pairs_z / (ms * 1e-3) / 1e12, 2)}
+    out["zigzag_64k_cp8"] = zz
+    del zq, zk, zv, zdo, zo, zl, zdq, zdk, zdv, zws
+    torch.cuda.empty_cache()
 
     # workspace sweep: peak bytes beyond inputs/outputs for one fwd+bwd, CP=8, rank 7
     sweep = []

@@ -15,4 +15,14 @@ from ._lib import (  # noqa: F401
     ring_attn_fwd_step,
     segment_mask_from_pos,
 )
-from .ring import RingWorkspace, ring_backward, ring_forward, ring_schedule  # noqa: F401
+from .ring import (  # noqa: F401
+    RingWorkspace,
+    ZigzagWorkspace,
+    ring_backward,
+    ring_backward_zigzag,
+    ring_forward,
+    ring_forward_zigzag,
+    ring_schedule,
+    zigzag_halves,
+    zigzag_pairs,
+)

@@ -12,7 +12,7 @@ arithmetic runs in the HIP library.
 from __future__ import annotations
 
 import math
-from typing import List, Optional, Sequence
+from typing import List, Optional, Sequence, Tuple
 
 import torch
 
@@ -115,3 +115,147 @@ def ring_backward(q_local: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chu
         if step_hook is not None:
             step_hook("bwd_step", i)
     return dq, list(dk_chunks), list(dv_chunks)
+
+
+# ---- load-balanced causal layout ----------------------------------------------------
+# With contiguous chunks and a causal mask, rank r has (r + 1/2) chunks' worth of
+# visible pairs, so the last rank sets the pace (aicassindra, "Transformer math: SP
+# math": the causal load-balance problem).  In the balanced ("zigzag") layout the
+# row is cut into 2*cp equal halves and rank r holds halves r and 2*cp-1-r (its
+# query, key and value rows, in that order); every rank then has the same number of
+# visible pairs, 2*cp*h^2 + h for halves of h tokens.  The ring is unchanged: at
+# step i rank r holds the K/V rows of rank (r - i) mod cp.  Each (query half, key
+# half) pair is one call of the step entry points with the halves' true global
+# offsets, so the causal rule and packed-row segment ids apply as everywhere else;
+# pairs in which every key lies after every query are skipped.
+
+def zigzag_halves(rank: int, cp: int) -> Tuple[int, int]:
+    """Half-chunk indices held by `rank` (each half covers h = S / (2 cp) tokens)."""
+    return rank, 2 * cp - 1 - rank
+
+
+def zigzag_pairs(rank: int, cp: int, h: int, causal: bool = True) -> List[Tuple[int, int, int, int]]:
+    """Live (ring step, KV rank, query half j, key half k) in ring order; j, k in {0, 1}
+    index the halves of `zigzag_halves`.  A pair is dropped when, under the causal
+    rule, its first key lies after its last query."""
+    qh = zigzag_halves(rank, cp)
+    out = []
+    for i, c in enumerate(ring_schedule(rank, cp)):
+        kh = zigzag_halves(c, cp)
+        for j in range(2):
+            for k in range(2):
+                if causal and kh[k] * h > qh[j] * h + h - 1:
+                    continue
+                out.append((i, c, j, k))
+    return out
+
+
+class ZigzagWorkspace:
+    """Device temporaries of the balanced-layout ring loops: per-half accumulators,
+    one step buffer, the backward's delta ([2, Hq, h]: one row block per half)."""
+
+    def __init__(self, h: int, Hq: int, d: int, device, backward: bool = False):
+        self.o_step = torch.empty((1, h, Hq, d), dtype=torch.float32, device=device)
+        self.lse_step = torch.empty((1, Hq, h), dtype=torch.float32, device=device)
+        self.o_acc = torch.empty((2, h, Hq, d), dtype=torch.float32, device=device)
+        self.delta = torch.empty((2, Hq, h), dtype=torch.float32, device=device) if backward else None
+
+    def nbytes(self) -> int:
+        ts = [self.o_step, self.lse_step, self.o_acc, self.delta]
+        return sum(t.numel() * t.element_size() for t in ts if t is not None)
+
+
+def _half(t: torch.Tensor, j: int, h: int) -> torch.Tensor:
+    return t[:, j * h:(j + 1) * h]
+
+
+def ring_forward_zigzag(q_local: torch.Tensor, k_ranks: Sequence[torch.Tensor], v_ranks: Sequence[torch.Tensor],
+                        rank: int, cp: int, *, causal: bool = True, scale: Optional[float] = None,
+                        seg_ids: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, workspace: Optional[ZigzagWorkspace] = None,
+                        stream=None, step_hook=None):
+    """Forward of one rank's share in the balanced layout.  Returns (O [1, 2h, Hq, d] in
+    q's dtype, LSE fp32 [2, Hq, h]: row block j = query half j).
+
+    q_local [1, 2h, Hq, d] holds the rank's two query halves; k_ranks/v_ranks: cp
+    tensors [1, 2h, Hkv, d], the K/V rows of each rank in the same layout; seg_ids
+    [1, S] int32 global segment ids or None.  Batch 1 (the half views must be
+    contiguous)."""
+    B, S2, Hq, d = q_local.shape
+    if B != 1 or S2 % 2:
+        raise ValueError("the balanced layout takes batch 1 and an even local length")
+    if len(k_ranks) != cp or len(v_ranks) != cp:
+        raise ValueError("need the K and V rows of every ring rank")
+    h = S2 // 2
+    sc = _scale(d, scale)
+    ws = workspace or ZigzagWorkspace(h, Hq, d, q_local.device)
+    if out is None:
+        out = torch.empty_like(q_local)
+    if lse is None:
+        lse = torch.empty((2, Hq, h), dtype=torch.float32, device=q_local.device)
+    qh = zigzag_halves(rank, cp)
+    pairs = zigzag_pairs(rank, cp, h, causal)
+    last_of = {j: max(n for n, p in enumerate(pairs) if p[2] == j) for j in range(2) if any(p[2] == j for p in pairs)}
+    seen = [False, False]
+    for n, (i, c, j, k) in enumerate(pairs):
+        kh = zigzag_halves(c, cp)
+        acc, lacc = ws.o_acc[j:j + 1], lse[j:j + 1]
+        first = not seen[j]
+        _lib.ring_attn_fwd_step(_half(q_local, j, h), _half(k_ranks[c], k, h), _half(v_ranks[c], k, h),
+                                acc if first else ws.o_step, lacc if first else ws.lse_step,
+                                q_offset=qh[j] * h, kv_offset=kh[k] * h, causal=causal, scale=sc,
+                                seg_ids=seg_ids, stream=stream)
+        if step_hook is not None:
+            step_hook("fwd_step", i)
+        last = last_of[j] == n
+        if not first:
+            _lib.lse_merge(acc, lacc, ws.o_step, ws.lse_step, o_out=_half(out, j, h) if last else None, stream=stream)
+            if step_hook is not None:
+                step_hook("merge", i)
+        elif last:
+            _lib.lse_merge(acc, lacc, None, None, o_out=_half(out, j, h), stream=stream)
+        seen[j] = True
+    for j in range(2):
+        if not seen[j]:  # no visible key at all (not reachable under the causal rule)
+            raise ValueError("a query half has no live key half")
+    return out, lse
+
+
+def ring_backward_zigzag(q_local: torch.Tensor, k_ranks: Sequence[torch.Tensor], v_ranks: Sequence[torch.Tensor],
+                         o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor, rank: int, cp: int, *,
+                         causal: bool = True, scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
+                         dq: Optional[torch.Tensor] = None, dk_ranks: Optional[Sequence[torch.Tensor]] = None,
+                         dv_ranks: Optional[Sequence[torch.Tensor]] = None,
+                         workspace: Optional[ZigzagWorkspace] = None, stream=None, step_hook=None):
+    """Backward of one rank's share in the balanced layout, from the forward's final O
+    and LSE [2, Hq, h].  Returns (dQ fp32 [1, 2h, Hq, d], dK list, dV list): dK[c]/dV[c]
+    [1, 2h, Hkv, d] fp32 hold this rank's contribution to rank c's K/V rows.  Given
+    accumulators are added to (+=)."""
+    B, S2, Hq, d = q_local.shape
+    if B != 1 or S2 % 2:
+        raise ValueError("the balanced layout takes batch 1 and an even local length")
+    h = S2 // 2
+    sc = _scale(d, scale)
+    dev = q_local.device
+    ws = workspace or ZigzagWorkspace(h, Hq, d, dev, backward=True)
+    if dq is None:
+        dq = torch.zeros((1, S2, Hq, d), dtype=torch.float32, device=dev)
+    if dk_ranks is None:
+        dk_ranks = [torch.zeros(k.shape, dtype=torch.float32, device=dev) for k in k_ranks]
+    if dv_ranks is None:
+        dv_ranks = [torch.zeros(v.shape, dtype=torch.float32, device=dev) for v in v_ranks]
+    for j in range(2):
+        _lib.ring_attn_bwd_preprocess(_half(o, j, h), _half(d_o, j, h), ws.delta[j:j + 1], stream=stream)
+    if step_hook is not None:
+        step_hook("bwd_preprocess", 0)
+    qh = zigzag_halves(rank, cp)
+    for i, c, j, k in zigzag_pairs(rank, cp, h, causal):
+        kh = zigzag_halves(c, cp)
+        _lib.ring_attn_bwd_step(_half(q_local, j, h), _half(k_ranks[c], k, h), _half(v_ranks[c], k, h),
+                                _half(d_o, j, h), lse[j:j + 1], ws.delta[j:j + 1], _half(dq, j, h),
+                                _half(dk_ranks[c], k, h), _half(dv_ranks[c], k, h),
+                                q_offset=qh[j] * h, kv_offset=kh[k] * h, causal=causal, scale=sc,
+                                seg_ids=seg_ids, stream=stream)
+        if step_hook is not None:
+            step_hook("bwd_step", i)
+    return dq, list(dk_ranks), list(dv_ranks)

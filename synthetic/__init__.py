@@ -10,4 +10,6 @@ from .workloads import (  # noqa: F401
     chunk_view,
     draw_packed_lengths,
     make_workload,
+    zigzag_indices,
+    zigzag_take,
 )

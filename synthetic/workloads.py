@@ -170,3 +170,19 @@ def make_workload(cfg: Config, q_chunks: Optional[list] = None, seed: Optional[i
 def chunk_view(x: np.ndarray, c: int, C: int) -> np.ndarray:
     """Rows [c*C, (c+1)*C) of a [B, S, ...] array (a view, no copy)."""
     return x[:, c * C:(c + 1) * C]
+
+
+def zigzag_indices(S: int, cp: int, rank: int) -> np.ndarray:
+    """Global token indices held by ``rank`` in the load-balanced causal layout: the
+    row is cut into 2*cp equal halves and the rank holds halves rank and
+    2*cp-1-rank, in that order.  Data placement only (used to lay out inputs)."""
+    if S % (2 * cp):
+        raise ValueError("S must be divisible by 2*cp")
+    h = S // (2 * cp)
+    lo, hi = rank, 2 * cp - 1 - rank
+    return np.concatenate([np.arange(lo * h, (lo + 1) * h), np.arange(hi * h, (hi + 1) * h)])
+
+
+def zigzag_take(x_full: np.ndarray, S: int, cp: int, rank: int) -> np.ndarray:
+    """Rows of a [B, S, ...] array held by ``rank`` in the load-balanced layout."""
+    return np.ascontiguousarray(x_full[:, zigzag_indices(S, cp, rank)])
