@@ -310,8 +310,9 @@ def packed_live_pairs(lengths, C, rank):
 
 def side_measurements(torch, ra, np, dev, CONFIGS, make_workload):
     """Forward TFLOP/s of the 8K and packed-16K shares, the segment-id kernel time, the
-    load-balanced (zigzag) 64K forward+backward of ranks 0 and 7, and the peak workspace
-    of one forward+backward at S = 16K..128K (CP=8, rank 7)."""
+    load-balanced (zigzag) 64K forward+backward of ranks 0 and 7, the 64K ring with
+    overlapped receives, and the peak workspace of one forward+backward at S = 16K..128K
+    (CP=8, rank 7)."""
     out = {}
 
     def ev_ms(fn, reps=5):
@@ -387,6 +388,49 @@ def side_measurements(torch, ra, np, dev, CONFIGS, make_workload):
         zz[f"rank{r}"] = {"ms": round(ms, 3), "tflops": round(14.0 * Hq * d * pairs_z / (ms * 1e-3) / 1e12, 2)}
     out["zigzag_64k_cp8"] = zz
     del zq, zk, zv, zdo, zo, zl, zdq, zdk, zdv, zws
+    torch.cuda.empty_cache()
+
+    # overlapped receives at the 64K shape (rank 7 of 8): chunks resident, received on a
+    # second stream into two slots while the previous step computes, or received on the
+    # compute stream (serialized); the transfer is a device-to-device copy standing for
+    # the peer's send
+    C, cp, Hq, Hkv, d = 8192, 8, 32, 8, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(4321)
+    oq = torch.randn((1, C, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    okc = [torch.randn((1, C, Hkv, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(cp)]
+    ovc = [torch.randn((1, C, Hkv, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(cp)]
+    odo = torch.randn((1, C, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    oo = torch.empty_like(oq)
+    ol = torch.empty((1, Hq, C), dtype=torch.float32, device=dev)
+    odq = torch.zeros((1, C, Hq, d), dtype=torch.float32, device=dev)
+    odk = [torch.zeros((1, C, Hkv, d), dtype=torch.float32, device=dev) for _ in range(cp)]
+    odv = [torch.zeros((1, C, Hkv, d), dtype=torch.float32, device=dev) for _ in range(cp)]
+    ows = ra.RingWorkspace(1, C, Hq, d, dev, backward=True)
+    osl = ra.RingSlots(okc[0], ovc[0], backward=True)
+    cur = torch.cuda.current_stream()
+    comm = torch.cuda.Stream(dev)
+
+    def resident():
+        ra.ring_forward(oq, okc, ovc, 7, cp, causal=True, out=oo, lse=ol, workspace=ows)
+        ra.ring_backward(oq, okc, ovc, oo, ol, odo, 7, cp, causal=True, dq=odq, dk_chunks=odk, dv_chunks=odv,
+                         delta=ows.delta)
+
+    def received(comm_stream):
+        ra.ring_forward_overlapped(oq, okc, ovc, 7, cp, causal=True, out=oo, lse=ol, workspace=ows, slots=osl,
+                                   stream=cur, comm_stream=comm_stream)
+        ra.ring_backward_overlapped(oq, okc, ovc, oo, ol, odo, 7, cp, causal=True, dq=odq, dk_chunks=odk,
+                                    dv_chunks=odv, delta=ows.delta, slots=osl, stream=cur, comm_stream=comm_stream)
+
+    t_res = ev_ms(resident, reps=3)
+    t_ovl = ev_ms(lambda: received(comm), reps=3)
+    t_ser = ev_ms(lambda: received(cur), reps=3)
+    per_step_bytes = 2 * C * Hkv * d * 2 + 2 * (2 * C * Hkv * d * 4)  # fwd K+V in; bwd K+V+dK+dV in, dK+dV out
+    out["overlapped_ring_64k_cp8_r7"] = {
+        "resident_ms": round(t_res, 3), "overlapped_ms": round(t_ovl, 3), "serialized_ms": round(t_ser, 3),
+        "received_bytes_per_step_fwd_plus_bwd": per_step_bytes,
+        "transfer_hidden_frac": round((t_ser - t_ovl) / (t_ser - t_res), 3) if t_ser > t_res else None}
+    del oq, okc, ovc, odo, oo, ol, odq, odk, odv, ows, osl
     torch.cuda.empty_cache()
 
     # workspace sweep: peak bytes beyond inputs/outputs for one fwd+bwd, CP=8, rank 7

@@ -13,14 +13,18 @@ from ._lib import (  # noqa: F401
     ring_attn_bwd_preprocess,
     ring_attn_bwd_step,
     ring_attn_fwd_step,
+    ring_recv_copy,
     segment_mask_from_pos,
 )
 from .ring import (  # noqa: F401
+    RingSlots,
     RingWorkspace,
     ZigzagWorkspace,
     ring_backward,
+    ring_backward_overlapped,
     ring_backward_zigzag,
     ring_forward,
+    ring_forward_overlapped,
     ring_forward_zigzag,
     ring_schedule,
     zigzag_halves,

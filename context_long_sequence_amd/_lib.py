@@ -26,6 +26,7 @@ EXPORTED = (
     "segment_mask_from_pos",
     "ring_attn_bwd_preprocess",
     "ring_attn_bwd_step",
+    "ring_recv_copy",
     "ra_status_string",
     "ra_last_error",
     "ra_abi_version",
@@ -78,8 +79,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.segment_mask_from_pos.argtypes = [i32, i64, vp, vp, vp]
     lib.ring_attn_bwd_preprocess.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.ring_attn_bwd_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
+    lib.ring_recv_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
     for fn in ("ring_attn_fwd_step", "lse_merge", "segment_mask_from_pos", "ring_attn_bwd_preprocess",
-               "ring_attn_bwd_step"):
+               "ring_attn_bwd_step", "ring_recv_copy"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.ra_status_string.argtypes = [ctypes.c_int]
     lib.ra_status_string.restype = ctypes.c_char_p
@@ -230,3 +232,14 @@ def ring_attn_bwd_step(q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, *, q_of
                                                         _ptr(lse), _ptr(delta), _ptr(seg_ids), seg_len,
                                                         _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc),
                                                         _stream(stream)))
+
+
+def ring_recv_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    """Receive `src` into `dst` (same shape and dtype, contiguous) with the DMA engines."""
+    if dst.shape != src.shape or dst.dtype != src.dtype:
+        raise ValueError(f"ring_recv_copy: {tuple(src.shape)} {src.dtype} into {tuple(dst.shape)} {dst.dtype}")
+    if not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("ring_recv_copy: tensors must be contiguous")
+    lib = load()
+    _check("ring_recv_copy", lib.ring_recv_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
+                                                _stream(stream)))

@@ -259,3 +259,157 @@ def ring_backward_zigzag(q_local: torch.Tensor, k_ranks: Sequence[torch.Tensor],
         if step_hook is not None:
             step_hook("bwd_step", i)
     return dq, list(dk_ranks), list(dv_ranks)
+
+
+# ---- overlapped receives --------------------------------------------------------------
+# A rank passes its K/V on while it attends to the chunk it holds (aicassindra,
+# "Transformer math: SP math": K/V blocks rotate around the ring; axolotl docs
+# "Sequence Parallelism", introduction: partial results are aggregated as chunks
+# pass around the ring).  Here the receive of the next step's chunk is a
+# device-to-device copy on the DMA engines (`ring_recv_copy`), from the buffer
+# standing for the peer's chunk into one of two receive slots, issued on a second
+# stream while the current step computes;
+# events order each copy after the step that last read its slot and before the step
+# that reads it.  In the backward the fp32 dK/dV partials travel with their chunk:
+# received with it, added to in place by the step, sent on after it.
+
+class RingSlots:
+    """Two receive slots for K and V (and, for the backward, the travelling dK/dV)."""
+
+    def __init__(self, k_like: torch.Tensor, v_like: torch.Tensor, backward: bool = False):
+        self.k = [torch.empty_like(k_like) for _ in range(2)]
+        self.v = [torch.empty_like(v_like) for _ in range(2)]
+        self.dk = [torch.empty(k_like.shape, dtype=torch.float32, device=k_like.device) for _ in range(2)] \
+            if backward else None
+        self.dv = [torch.empty(v_like.shape, dtype=torch.float32, device=v_like.device) for _ in range(2)] \
+            if backward else None
+
+    def nbytes(self) -> int:
+        ts = self.k + self.v + (self.dk or []) + (self.dv or [])
+        return sum(t.numel() * t.element_size() for t in ts)
+
+
+def _streams(stream, comm_stream, device):
+    compute = torch.cuda.current_stream(device) if stream is None else stream
+    if not isinstance(compute, torch.cuda.Stream):
+        raise TypeError("the overlapped ring needs torch.cuda.Stream objects")
+    comm = torch.cuda.Stream(device) if comm_stream is None else comm_stream
+    return compute, comm
+
+
+def ring_forward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Tensor],
+                            v_chunks: Sequence[torch.Tensor], rank: int, cp: int, *, causal: bool = True,
+                            scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            workspace: Optional[RingWorkspace] = None, slots: Optional[RingSlots] = None,
+                            stream=None, comm_stream=None):
+    """`ring_forward` with the chunk of step i+1 received while step i computes.
+    Same kernels in the same order, so the results are bit-identical."""
+    B, C, Hq, d = q_local.shape
+    sc = _scale(d, scale)
+    dev = q_local.device
+    compute, comm = _streams(stream, comm_stream, dev)
+    ws = workspace or RingWorkspace(B, C, Hq, d, dev)
+    sl = slots or RingSlots(k_chunks[0], v_chunks[0])
+    if out is None:
+        out = torch.empty_like(q_local)
+    if lse is None:
+        lse = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
+    sched = ring_schedule(rank, cp)
+    comm.wait_stream(compute)  # the chunks may have been produced on the compute stream
+    received: List[Optional[torch.cuda.Event]] = [None, None]
+    released: List[Optional[torch.cuda.Event]] = [None, None]
+
+    def receive(i):
+        s, c = i % 2, sched[i]
+        if released[s] is not None:
+            comm.wait_event(released[s])
+        _lib.ring_recv_copy(sl.k[s], k_chunks[c], stream=comm)
+        _lib.ring_recv_copy(sl.v[s], v_chunks[c], stream=comm)
+        received[s] = torch.cuda.Event()
+        received[s].record(comm)
+
+    o_acc = ws.o_acc
+    for i, c in enumerate(sched):
+        if i + 1 < cp:
+            receive(i + 1)
+        if i == 0:
+            kc, vc = k_chunks[c], v_chunks[c]  # the rank's own chunk needs no receive
+        else:
+            compute.wait_event(received[i % 2])
+            kc, vc = sl.k[i % 2], sl.v[i % 2]
+        first, last = i == 0, i == cp - 1
+        _lib.ring_attn_fwd_step(q_local, kc, vc, o_acc if first else ws.o_step, lse if first else ws.lse_step,
+                                q_offset=rank * C, kv_offset=c * kc.shape[1], causal=causal, scale=sc,
+                                seg_ids=seg_ids, stream=compute)
+        if i > 0:
+            released[i % 2] = torch.cuda.Event()
+            released[i % 2].record(compute)
+        if not first:
+            _lib.lse_merge(o_acc, lse, ws.o_step, ws.lse_step, o_out=out if last else None, stream=compute)
+        elif last:
+            _lib.lse_merge(o_acc, lse, None, None, o_out=out, stream=compute)
+    return out, lse
+
+
+def ring_backward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Tensor],
+                             v_chunks: Sequence[torch.Tensor], o: torch.Tensor, lse: torch.Tensor,
+                             d_o: torch.Tensor, rank: int, cp: int, *, causal: bool = True,
+                             scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
+                             dq: Optional[torch.Tensor] = None, dk_chunks: Optional[Sequence[torch.Tensor]] = None,
+                             dv_chunks: Optional[Sequence[torch.Tensor]] = None, delta: Optional[torch.Tensor] = None,
+                             slots: Optional[RingSlots] = None, stream=None, comm_stream=None):
+    """`ring_backward` with receives (K, V and the travelling dK/dV partial of the next
+    chunk) overlapped with the current step, and each partial sent on after its step.
+    dk_chunks[c]/dv_chunks[c] stand for the partial that arrives with chunk c; on
+    return they hold it plus this rank's contribution, bit-identical to
+    `ring_backward`."""
+    B, C, Hq, d = q_local.shape
+    sc = _scale(d, scale)
+    dev = q_local.device
+    compute, comm = _streams(stream, comm_stream, dev)
+    sl = slots or RingSlots(k_chunks[0], v_chunks[0], backward=True)
+    if sl.dk is None:
+        raise ValueError("the backward needs slots with dK/dV buffers")
+    if dq is None:
+        dq = torch.zeros((B, C, Hq, d), dtype=torch.float32, device=dev)
+    if dk_chunks is None:
+        dk_chunks = [torch.zeros(k.shape, dtype=torch.float32, device=dev) for k in k_chunks]
+    if dv_chunks is None:
+        dv_chunks = [torch.zeros(v.shape, dtype=torch.float32, device=dev) for v in v_chunks]
+    if delta is None:
+        delta = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
+    sched = ring_schedule(rank, cp)
+    comm.wait_stream(compute)
+    _lib.ring_attn_bwd_preprocess(o, d_o, delta, stream=compute)
+    received: List[Optional[torch.cuda.Event]] = [None, None]
+
+    def receive(i):
+        # in comm-stream order after the send of step i-2, which used this slot
+        s, c = i % 2, sched[i]
+        for dst, src in ((sl.k[s], k_chunks[c]), (sl.v[s], v_chunks[c]), (sl.dk[s], dk_chunks[c]),
+                         (sl.dv[s], dv_chunks[c])):
+            _lib.ring_recv_copy(dst, src, stream=comm)
+        received[s] = torch.cuda.Event()
+        received[s].record(comm)
+
+    for i, c in enumerate(sched):
+        if i + 1 < cp:
+            receive(i + 1)
+        if i == 0:
+            kc, vc, dkc, dvc = k_chunks[c], v_chunks[c], dk_chunks[c], dv_chunks[c]
+        else:
+            s = i % 2
+            compute.wait_event(received[s])
+            kc, vc, dkc, dvc = sl.k[s], sl.v[s], sl.dk[s], sl.dv[s]
+        _lib.ring_attn_bwd_step(q_local, kc, vc, d_o, lse, delta, dq, dkc, dvc,
+                                q_offset=rank * C, kv_offset=c * kc.shape[1], causal=causal, scale=sc,
+                                seg_ids=seg_ids, stream=compute)
+        if i > 0:  # send the partial on once the step has added to it
+            done = torch.cuda.Event()
+            done.record(compute)
+            comm.wait_event(done)
+            _lib.ring_recv_copy(dk_chunks[c], dkc, stream=comm)
+            _lib.ring_recv_copy(dv_chunks[c], dvc, stream=comm)
+    compute.wait_stream(comm)  # the last sends are part of the result
+    return dq, list(dk_chunks), list(dv_chunks)

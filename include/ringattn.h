@@ -41,6 +41,7 @@
 #ifndef RINGATTN_H
 #define RINGATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -155,13 +156,31 @@ ra_status ring_attn_bwd_step(const ra_shape* shape, const void* q, const void* k
                              const int32_t* seg_ids, int64_t seg_len, float* dq_acc,
                              float* dk_acc, float* dv_acc, void* stream);
 
+/*
+ * ring_recv_copy — the transfer of one ring step, on one GPU: copies `bytes` bytes
+ * from `src` (the buffer that stands for the peer's K/V chunk, or for a travelling
+ * dK/dV partial) to `dst` (a receive slot) on `stream`, with the DMA engines
+ * (hipMemcpyDeviceToDeviceNoCU), so the copy takes no compute units from the step
+ * kernels running on another stream.  K/V rotate around the ring while each rank
+ * attends to the chunk it holds (aicassindra, "Transformer math: SP math",
+ * section on context parallelism; axolotl docs "Sequence Parallelism",
+ * introduction).
+ *
+ *  dst, src  device pointers of the same device, regions of `bytes` bytes that do
+ *            not overlap; bytes == 0 is a no-op.
+ * Asynchronous: ordering against other streams is the caller's (events).
+ * Errors: RA_ERR_INVALID_ARGUMENT for NULL pointers (with bytes > 0);
+ * RA_ERR_HIP if the runtime rejects the copy.
+ */
+ra_status ring_recv_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* ra_status_string(ra_status status);
 
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* ra_last_error(void);
 
-/* Library ABI version: 1. */
+/* Library ABI version: 2 (2 added ring_recv_copy). */
 int32_t ra_abi_version(void);
 
 #ifdef __cplusplus

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ra_abi_version() == 1
+    assert lib.ra_abi_version() == 2
     assert lib.ra_status_string(0) == b"RA_OK"
     assert lib.ra_status_string(2) == b"RA_ERR_UNSUPPORTED"
 
@@ -99,3 +99,9 @@ def test_merge_segment_preprocess_validation(lib):
     assert lib.segment_mask_from_pos(1, 1 << 40, FAKE, FAKE, None) == 1
     assert lib.ring_attn_bwd_preprocess(1, 4, 4, 96, 1, FAKE, FAKE, FAKE, None) == 2
     assert lib.ring_attn_bwd_preprocess(1, 4, 4, 128, 5, FAKE, FAKE, FAKE, None) == 2
+
+
+def test_recv_copy_rejects_null_pointers(lib):
+    assert lib.ring_recv_copy(None, None, 16, None) == 1  # RA_ERR_INVALID_ARGUMENT
+    assert b"non-NULL" in lib.ra_last_error()
+    assert lib.ring_recv_copy(None, None, 0, None) == 0  # zero bytes: nothing to do
