@@ -311,7 +311,7 @@ def packed_live_pairs(lengths, C, rank):
 def side_measurements(torch, ra, np, dev, CONFIGS, make_workload):
     """Forward TFLOP/s of the 8K and packed-16K shares, the segment-id kernel time, the
     load-balanced (zigzag) 64K forward+backward of ranks 0 and 7, the 64K ring with
-    overlapped receives, and the peak workspace of one forward+backward at S = 16K..128K
+    overlapped receives, the head-sharded and gathered-KV 64K shares, and the peak workspace of one forward+backward at S = 16K..128K
     (CP=8, rank 7)."""
     out = {}
 
@@ -431,6 +431,62 @@ def side_measurements(torch, ra, np, dev, CONFIGS, make_workload):
         "received_bytes_per_step_fwd_plus_bwd": per_step_bytes,
         "transfer_hidden_frac": round((t_ser - t_ovl) / (t_ser - t_res), 3) if t_ser > t_res else None}
     del oq, okc, ovc, odo, oo, ol, odq, odk, odv, ows, osl
+    torch.cuda.empty_cache()
+
+    # the same 64K attention, other shares: head-sharded (Ulysses: 4 of 32 query heads and
+    # 1 of 8 KV heads over all 65536 tokens) and gathered-KV (rank 7's chunk against the
+    # gathered row, gather and gradient scatter included)
+    S, cp, d = 65536, 8, 128
+    C = S // cp
+    g = torch.Generator(device=dev)
+    g.manual_seed(999)
+    uq = torch.randn((1, S, 4, d), generator=g, device=dev).to(torch.bfloat16)
+    uk = torch.randn((1, S, 1, d), generator=g, device=dev).to(torch.bfloat16)
+    uv = torch.randn((1, S, 1, d), generator=g, device=dev).to(torch.bfloat16)
+    udo = torch.randn((1, S, 4, d), generator=g, device=dev).to(torch.bfloat16)
+    uo, ul = torch.empty_like(uq), torch.empty((1, 4, S), dtype=torch.float32, device=dev)
+    uo32 = torch.empty((1, S, 4, d), dtype=torch.float32, device=dev)
+    udq = torch.zeros((1, S, 4, d), dtype=torch.float32, device=dev)
+    udk = torch.zeros((1, S, 1, d), dtype=torch.float32, device=dev)
+    udv = torch.zeros_like(udk)
+    udelta = torch.empty((1, 4, S), dtype=torch.float32, device=dev)
+
+    def uly():
+        ra.ulysses_forward(uq, uk, uv, causal=True, out=uo, lse=ul, o_f32=uo32)
+        ra.ulysses_backward(uq, uk, uv, uo, ul, udo, causal=True, dq=udq, dk=udk, dv=udv, delta=udelta)
+
+    ums = ev_ms(uly, reps=3)
+    upairs = S * (S + 1) // 2
+    out["ulysses_64k_h4_of_32"] = {"ms": round(ums, 3), "tflops": round(14.0 * 4 * d * upairs / (ums * 1e-3) / 1e12, 2)}
+    del uq, uk, uv, udo, uo, ul, uo32, udq, udk, udv, udelta
+
+    gq = torch.randn((1, C, 32, d), generator=g, device=dev).to(torch.bfloat16)
+    gks = [torch.randn((1, C, 8, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(cp)]
+    gvs = [torch.randn((1, C, 8, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(cp)]
+    gdo = torch.randn((1, C, 32, d), generator=g, device=dev).to(torch.bfloat16)
+    gk_all = torch.empty((1, S, 8, d), dtype=torch.bfloat16, device=dev)
+    gv_all = torch.empty_like(gk_all)
+    go, gl = torch.empty_like(gq), torch.empty((1, 32, C), dtype=torch.float32, device=dev)
+    go32 = torch.empty((1, C, 32, d), dtype=torch.float32, device=dev)
+    gdq = torch.zeros((1, C, 32, d), dtype=torch.float32, device=dev)
+    gdk_all = torch.zeros((1, S, 8, d), dtype=torch.float32, device=dev)
+    gdv_all = torch.zeros_like(gdk_all)
+    gdks = [torch.empty((1, C, 8, d), dtype=torch.float32, device=dev) for _ in range(cp)]
+    gdvs = [torch.empty((1, C, 8, d), dtype=torch.float32, device=dev) for _ in range(cp)]
+    gdelta = torch.empty((1, 32, C), dtype=torch.float32, device=dev)
+
+    def gat():
+        ra.gather_kv(gks, gvs, gk_all, gv_all)
+        ra.gathered_forward(gq, gk_all, gv_all, cp - 1, causal=True, out=go, lse=gl, o_f32=go32)
+        ra.gathered_backward(gq, gk_all, gv_all, go, gl, gdo, cp - 1, causal=True, dq=gdq, dk_all=gdk_all,
+                             dv_all=gdv_all, delta=gdelta)
+        ra.scatter_dkv(gdk_all, gdv_all, gdks, gdvs)
+
+    gms = ev_ms(gat, reps=3)
+    gpairs = live_pairs_causal(C, cp - 1)
+    out["gathered_kv_64k_cp8_r7"] = {"ms": round(gms, 3),
+                                     "tflops": round(14.0 * 32 * d * gpairs / (gms * 1e-3) / 1e12, 2)}
+    del gq, gks, gvs, gdo, gk_all, gv_all, go, gl, go32, gdq, gdk_all, gdv_all, gdks, gdvs, gdelta
     torch.cuda.empty_cache()
 
     # workspace sweep: peak bytes beyond inputs/outputs for one fwd+bwd, CP=8, rank 7

@@ -29,4 +29,10 @@ from .ring import (  # noqa: F401
     ring_schedule,
     zigzag_halves,
     zigzag_pairs,
+    gather_kv,
+    gathered_backward,
+    gathered_forward,
+    scatter_dkv,
+    ulysses_backward,
+    ulysses_forward,
 )

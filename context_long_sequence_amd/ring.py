@@ -413,3 +413,140 @@ def ring_backward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Ten
             _lib.ring_recv_copy(dv_chunks[c], dvc, stream=comm)
     compute.wait_stream(comm)  # the last sends are part of the result
     return dq, list(dk_chunks), list(dv_chunks)
+
+
+# ---- head-sharded share (Ulysses) ---------------------------------------------------
+# Instead of cutting the sequence, a rank holds Hq/cp query heads and Hkv/cp KV heads
+# of the whole row (aicassindra, "Transformer math: SP math", the head-sharded
+# alternative to the ring; the all-to-all that moves a rank's sequence chunk into
+# this layout and back is the multi-GPU part, left out).  Its share is plain masked
+# attention over the full row: one forward step call and one backward step call
+# with offsets 0 — the same kernels at a different shape, no merges.
+
+def ulysses_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True,
+                    scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    o_f32: Optional[torch.Tensor] = None, stream=None):
+    """q [B, S, Hq', d], k/v [B, S, Hkv', d] (the rank's heads of the whole row).
+    Returns (O in q's dtype, LSE fp32 [B, Hq', S])."""
+    B, S, Hq, d = q.shape
+    sc = _scale(d, scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    if o_f32 is None:
+        o_f32 = torch.empty((B, S, Hq, d), dtype=torch.float32, device=dev)
+    _lib.ring_attn_fwd_step(q, k, v, o_f32, lse, q_offset=0, kv_offset=0, causal=causal, scale=sc,
+                            seg_ids=seg_ids, stream=stream)
+    _lib.lse_merge(o_f32, lse, None, None, o_out=out, stream=stream)
+    return out, lse
+
+
+def ulysses_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                     d_o: torch.Tensor, *, causal: bool = True, scale: Optional[float] = None,
+                     seg_ids: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
+                     dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                     delta: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of `ulysses_forward` (fp32; given accumulators are added to)."""
+    B, S, Hq, d = q.shape
+    sc = _scale(d, scale)
+    dev = q.device
+    if dq is None:
+        dq = torch.zeros((B, S, Hq, d), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.zeros(v.shape, dtype=torch.float32, device=dev)
+    if delta is None:
+        delta = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    _lib.ring_attn_bwd_preprocess(o, d_o, delta, stream=stream)
+    _lib.ring_attn_bwd_step(q, k, v, d_o, lse, delta, dq, dk, dv, q_offset=0, kv_offset=0, causal=causal,
+                            scale=sc, seg_ids=seg_ids, stream=stream)
+    return dq, dk, dv
+
+
+# ---- gathered-KV share (llama3-style) ------------------------------------------------
+# The alternative to the ring that packing-aware trainers use by default (axolotl docs
+# "Sequence Parallelism", the ring_attn_func options): every rank gathers the K/V of
+# the whole row, then its contiguous query chunk attends to it once, segment ids
+# handling packed samples.  `heads_k_stride` there bounds the gathered memory by
+# gathering a few KV heads per round; with 288 GB of HBM per GPU the whole row's K/V
+# (256 MiB at 64K, 8 KV heads, d = 128) is gathered at once.  On one GPU the gather
+# is cp device-to-device copies (DMA engines) of the chunk buffers into one [B, S,
+# Hkv, d] buffer; the backward's reduce-scatter returns each chunk's dK/dV rows to
+# the chunk accumulators the same way.
+
+def gather_kv(k_chunks: Sequence[torch.Tensor], v_chunks: Sequence[torch.Tensor],
+              k_all: Optional[torch.Tensor] = None, v_all: Optional[torch.Tensor] = None, stream=None):
+    """Concatenate the chunks along the row into k_all/v_all [B, S, Hkv, d] (batch 1: the
+    chunk rows of one batch row are contiguous in the gathered buffer)."""
+    B, C, Hkv, d = k_chunks[0].shape
+    if B != 1:
+        raise ValueError("the gathered share takes batch 1")
+    cp = len(k_chunks)
+    if k_all is None:
+        k_all = torch.empty((1, cp * C, Hkv, d), dtype=k_chunks[0].dtype, device=k_chunks[0].device)
+    if v_all is None:
+        v_all = torch.empty((1, cp * C, Hkv, d), dtype=v_chunks[0].dtype, device=v_chunks[0].device)
+    for c in range(cp):
+        _lib.ring_recv_copy(k_all[:, c * C:(c + 1) * C], k_chunks[c], stream=stream)
+        _lib.ring_recv_copy(v_all[:, c * C:(c + 1) * C], v_chunks[c], stream=stream)
+    return k_all, v_all
+
+
+def gathered_forward(q_local: torch.Tensor, k_all: torch.Tensor, v_all: torch.Tensor, rank: int, *,
+                     causal: bool = True, scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     o_f32: Optional[torch.Tensor] = None, stream=None):
+    """The rank's contiguous query chunk q_local [B, C, Hq, d] against the gathered row
+    k_all/v_all [B, S, Hkv, d].  Returns (O in q's dtype, LSE fp32 [B, Hq, C])."""
+    B, C, Hq, d = q_local.shape
+    sc = _scale(d, scale)
+    dev = q_local.device
+    if out is None:
+        out = torch.empty_like(q_local)
+    if lse is None:
+        lse = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
+    if o_f32 is None:
+        o_f32 = torch.empty((B, C, Hq, d), dtype=torch.float32, device=dev)
+    _lib.ring_attn_fwd_step(q_local, k_all, v_all, o_f32, lse, q_offset=rank * C, kv_offset=0, causal=causal,
+                            scale=sc, seg_ids=seg_ids, stream=stream)
+    _lib.lse_merge(o_f32, lse, None, None, o_out=out, stream=stream)
+    return out, lse
+
+
+def gathered_backward(q_local: torch.Tensor, k_all: torch.Tensor, v_all: torch.Tensor, o: torch.Tensor,
+                      lse: torch.Tensor, d_o: torch.Tensor, rank: int, *, causal: bool = True,
+                      scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
+                      dq: Optional[torch.Tensor] = None, dk_all: Optional[torch.Tensor] = None,
+                      dv_all: Optional[torch.Tensor] = None, delta: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of `gathered_forward`: dQ [B, C, Hq, d] and this rank's contribution to
+    the whole row's dK/dV [B, S, Hkv, d] (fp32; given accumulators are added to).  Rows
+    [c*C, (c+1)*C) of dk_all/dv_all belong to chunk c (`scatter_dkv` returns them)."""
+    B, C, Hq, d = q_local.shape
+    sc = _scale(d, scale)
+    dev = q_local.device
+    if dq is None:
+        dq = torch.zeros((B, C, Hq, d), dtype=torch.float32, device=dev)
+    if dk_all is None:
+        dk_all = torch.zeros(k_all.shape, dtype=torch.float32, device=dev)
+    if dv_all is None:
+        dv_all = torch.zeros(v_all.shape, dtype=torch.float32, device=dev)
+    if delta is None:
+        delta = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
+    _lib.ring_attn_bwd_preprocess(o, d_o, delta, stream=stream)
+    _lib.ring_attn_bwd_step(q_local, k_all, v_all, d_o, lse, delta, dq, dk_all, dv_all, q_offset=rank * C,
+                            kv_offset=0, causal=causal, scale=sc, seg_ids=seg_ids, stream=stream)
+    return dq, dk_all, dv_all
+
+
+def scatter_dkv(dk_all: torch.Tensor, dv_all: torch.Tensor, dk_chunks: Sequence[torch.Tensor],
+                dv_chunks: Sequence[torch.Tensor], stream=None) -> None:
+    """Copy row block c of the gathered-row gradients into the chunk accumulators
+    dk_chunks[c]/dv_chunks[c] (the reduce-scatter's data movement for this rank)."""
+    C = dk_chunks[0].shape[1]
+    for c in range(len(dk_chunks)):
+        _lib.ring_recv_copy(dk_chunks[c], dk_all[:, c * C:(c + 1) * C], stream=stream)
+        _lib.ring_recv_copy(dv_chunks[c], dv_all[:, c * C:(c + 1) * C], stream=stream)
