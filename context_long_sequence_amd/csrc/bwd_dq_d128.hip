@@ -16,7 +16,12 @@ constexpr int kTile = kD128Tile;
 // ------------------------------------------------------------------------------------
 // dQ: 4 waves x 32 queries of one query head; walks the key tiles of the chunk.
 // ------------------------------------------------------------------------------------
-constexpr int kDqWaves = 4;
+#ifndef RA_DQ_WAVES
+#define RA_DQ_WAVES 4  // waves (x 32 queries) per dQ workgroup: 4 or 8
+#endif
+constexpr int kDqWaves = RA_DQ_WAVES;
+static_assert(kDqWaves == 4 || kDqWaves == 8, "a 32-row tile is 8 blocks of 1 KiB, split evenly over the waves");
+constexpr int kDqBlocks = 8 / kDqWaves;  // 1 KiB blocks of a tile copied by each wave
 constexpr int kDqThreads = 64 * kDqWaves;
 
 template <bool kSeg>
@@ -106,14 +111,14 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
 
-  // Copies: 32 rows x 256 bytes per tile and tensor = 8 blocks of 1 KiB, two per
+  // Copies: 32 rows x 256 bytes per tile and tensor = 8 blocks of 1 KiB, 8 / waves per
   // wave; lane l of a block writes 16 bytes at 16*l, so it fetches the global chunk
   // that the swizzle puts there.  Raw buffer loads with a per-tile descriptor whose
   // range ends at the chunk's last key: rows past it read as zeros (and are masked).
-  uint32_t coff[2];
+  uint32_t coff[kDqBlocks];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int row = (2 * wave + r) * 4 + (lane >> 4);
+  for (int r = 0; r < kDqBlocks; ++r) {
+    const int row = (kDqBlocks * wave + r) * 4 + (lane >> 4);
     coff[r] = (uint32_t)(row * kv_rb + ((lane & 15) ^ swz(row)) * 16);
   }
   auto issue = [&](int t, __bf16* kdst, __bf16* vdst) {
@@ -121,14 +126,14 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
     const int64_t bytes = (int64_t)(a.Sk - 1 - k0) * kv_rb + kD * 2;
     const buffer_rsrc rk = make_rsrc(kbase + (int64_t)k0 * kv_rb, bytes);
     const buffer_rsrc rv = make_rsrc(vbase + (int64_t)k0 * kv_rb, bytes);
-    char* dk = reinterpret_cast<char*>(kdst) + 2 * wave * 1024;
-    char* dv = reinterpret_cast<char*>(vdst) + 2 * wave * 1024;
+    char* dk = reinterpret_cast<char*>(kdst) + kDqBlocks * wave * 1024;
+    char* dv = reinterpret_cast<char*>(vdst) + kDqBlocks * wave * 1024;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) buffer_load_lds16(rk, dk + r * 1024, coff[r]);
+    for (int r = 0; r < kDqBlocks; ++r) buffer_load_lds16(rk, dk + r * 1024, coff[r]);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) buffer_load_lds16(rv, dv + r * 1024, coff[r]);
+    for (int r = 0; r < kDqBlocks; ++r) buffer_load_lds16(rv, dv + r * 1024, coff[r]);
   };
-  constexpr int kCopiesPerTile = 4;  // per wave: K and V, two blocks each
+  constexpr int kCopiesPerTile = 2 * kDqBlocks;  // per wave: K and V
 
   // LDS operand offsets.  K and V rows (A of S^T = K Q^T, dP^T = V dO^T): row
   // key_of_row(col), 16-byte chunk 2s+half, i.e. kA ^ (s << 5).  K^T (A of
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
   // statements keep the compiler from moving LDS accesses across it.
   auto step = [&](int t, const __bf16* kc, const __bf16* vc, __bf16* kn, __bf16* vn) {
     if (t + 1 < kt_end)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesPerTile);  // vmcnt(4): tile t+1 may stay in flight
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesPerTile);  // tile t+1 may stay in flight
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     asm volatile("" ::: "memory");

@@ -361,22 +361,25 @@ __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a) {
 
 
 // ------------------------------------------------------------------------------------
-// bf16, head_dim 128: the hot shape.  One workgroup = 4 waves x 32 queries of one
-// query head.  K and V tiles of 32 keys are copied global -> LDS (swizzled,
-// row-major) without staging registers into two rings of three slots, K three
+// bf16, head_dim 128: the hot shape.  One workgroup = 4 or 8 waves x 32 queries of
+// one query head.  K and V tiles of 32
+// keys are copied global -> LDS (swizzled, row-major) without staging registers
+// into two rings of three slots, K three
 // tiles and V two tiles ahead of their use, so a copy has two steps to land.  V^T
 // operands come from transposing LDS reads.  The scores of tile t+1 are issued
 // before the softmax of tile t, so the matrix cores work while the vector ALUs do
 // the softmax.
 // ------------------------------------------------------------------------------------
-constexpr int kD128Waves = 4;
-constexpr int kD128Threads = 64 * kD128Waves;
-constexpr int kD128BM = 32 * kD128Waves;  // queries per workgroup
-constexpr int kD128BN = 32;               // keys per tile
+constexpr int kD128BN = 32;  // keys per tile
 
-template <bool kSeg>
-__global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) {
-  constexpr int D = 128, BN = kD128BN, BM = kD128BM;
+// NW = 4 or 8 waves (x 32 queries) per workgroup: with 8, two waves per SIMD share
+// each K/V tile copy (half the tile traffic per query); 4 keeps more workgroups for
+// small grids.
+template <bool kSeg, int NW>
+__global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
+  static_assert(NW == 4 || NW == 8, "a 32-row tile is 8 blocks of 1 KiB, split evenly over the waves");
+  constexpr int D = 128, BN = kD128BN, BM = 32 * NW;
+  constexpr int kD128Blocks = 8 / NW;  // 1 KiB blocks of a tile copied by each wave
   // Each slot its own array, so the compiler can tell the copies in flight from
   // the tiles being read.
   __shared__ __attribute__((aligned(1024))) __bf16 ks0[BN * D];
@@ -464,25 +467,25 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
     causal_lim = (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, c));
   }
 
-  // Copies: 32 rows x 256 bytes per tile = 8 blocks of 1 KiB, two per wave; lane
+  // Copies: 32 rows x 256 bytes per tile = 8 blocks of 1 KiB, 8 / waves per wave; lane
   // l of a block writes 16 bytes at 16*l, so it fetches the global chunk that the
   // swizzle puts there.  Raw buffer loads with a per-tile descriptor whose range
   // ends at the chunk's last key: rows past it read as zeros (and are masked).
-  uint32_t coff[2];
+  uint32_t coff[kD128Blocks];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int row = (2 * wave + r) * 4 + (lane >> 4);
+  for (int r = 0; r < kD128Blocks; ++r) {
+    const int row = (kD128Blocks * wave + r) * 4 + (lane >> 4);
     coff[r] = (uint32_t)(row * kv_rb + ((lane & 15) ^ swz(row)) * 16);
   }
   auto copy_tile = [&](const char* base, int t, __bf16* dst) {
     const int k0 = t * BN;
     const int64_t bytes = (int64_t)(a.Sk - 1 - k0) * kv_rb + D * 2;  // through the last key's row
     const buffer_rsrc rs = make_rsrc(base + (int64_t)k0 * kv_rb, bytes);
-    char* d = reinterpret_cast<char*>(dst) + 2 * wave * 1024;
+    char* d = reinterpret_cast<char*>(dst) + kD128Blocks * wave * 1024;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) buffer_load_lds16(rs, d + r * 1024, coff[r]);
+    for (int r = 0; r < kD128Blocks; ++r) buffer_load_lds16(rs, d + r * 1024, coff[r]);
   };
-  constexpr int kCopiesPerTile = 2;  // per wave and tensor
+  constexpr int kCopiesPerTile = kD128Blocks;  // per wave and tensor
 
   // LDS operand offsets.  K (A of S^T): row key_of_row(col), 16-byte chunk 2s+half,
   // i.e. kA ^ (s << 5).  V^T (A of O^T += V^T P^T) via transposing reads of rows
@@ -594,9 +597,9 @@ __global__ __launch_bounds__(kD128Threads) void fwd_step_d128_kernel(FwdArgs a) 
   f32x16 s_next = f32x16{};
   auto step = [&](int t, const __bf16* kq, const __bf16* vc, __bf16* kn, __bf16* vn) {
     if (t + 2 < kt_end)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kCopiesPerTile));  // vmcnt(4)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kCopiesPerTile));  // both tensors of the last step in flight
     else if (t + 1 < kt_end)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesPerTile);  // vmcnt(2)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesPerTile);  // its V copies in flight
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     asm volatile("" ::: "memory");
@@ -668,13 +671,19 @@ ra_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
   const int64_t n_wg = (int64_t)args.B * args.Hq * args.n_qtiles;
   if (n_wg > INT32_MAX) return fail(RA_ERR_INVALID_ARGUMENT, "too many workgroups");
   if constexpr (std::is_same<T, __bf16>::value && D == 128) {
+    // 8-wave workgroups when the grid still gives every CU (256 on MI355X) four of
+    // them and no segment test runs (packed rows keep the finer 128-query tiles).
+    const int64_t n8 = (int64_t)args.B * args.Hq * ((args.Sq + 255) / 256);
+    const bool wide = args.seg == nullptr && n8 >= 4 * 256;
     FwdArgs a2 = args;
-    a2.n_qtiles = (args.Sq + kD128BM - 1) / kD128BM;
-    const int64_t n2 = (int64_t)args.B * args.Hq * a2.n_qtiles;
+    a2.n_qtiles = (args.Sq + (wide ? 255 : 127)) / (wide ? 256 : 128);
+    const unsigned n2 = (unsigned)((int64_t)args.B * args.Hq * a2.n_qtiles);
     if (args.seg != nullptr)
-      hipLaunchKernelGGL((fwd_step_d128_kernel<true>), dim3((unsigned)n2), dim3(kD128Threads), 0, stream, a2);
+      hipLaunchKernelGGL((fwd_step_d128_kernel<true, 4>), dim3(n2), dim3(256), 0, stream, a2);
+    else if (wide)
+      hipLaunchKernelGGL((fwd_step_d128_kernel<false, 8>), dim3(n2), dim3(512), 0, stream, a2);
     else
-      hipLaunchKernelGGL((fwd_step_d128_kernel<false>), dim3((unsigned)n2), dim3(kD128Threads), 0, stream, a2);
+      hipLaunchKernelGGL((fwd_step_d128_kernel<false, 4>), dim3(n2), dim3(256), 0, stream, a2);
     return check_launch("ring_attn_fwd_step");
   }
   if (args.seg != nullptr)

@@ -226,6 +226,49 @@ def test_bwd_step(case):
     report("bwd_step", case=case, **errs)
 
 
+WIDE_CASES = [
+    # (Sq, Sk, q_off, kv_off, causal): 128 query heads x ceil(Sq / 256) >= 1024 query tiles
+    # of 256 rows, the grid size at which the bf16 d=128 forward uses 8-wave workgroups.
+    (1900, 2100, 2100, 2100, True),   # diagonal chunk, ragged tails on both sides
+    (1900, 2100, 2100, 0, True),      # earlier chunk: every block fully visible
+    (2048, 1500, 900, 1200, True),    # partly in the future: some rows see nothing
+    (2000, 333, 0, 0, False),         # non-causal, short chunk
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_fwd_step_wide_grid(case):
+    """A forward step on a grid large enough for the 8-wave workgroup variant: full
+    comparison with the oracle on a subset of query heads (each head is an
+    independent attention problem over its own KV head)."""
+    ra = lib()
+    Sq, Sk, q_off, kv_off, causal = case
+    B, Hq, Hkv, d = 1, 128, 8, 128
+    rng = np.random.default_rng(Sq + 7 * Sk + q_off)
+    q, k, v = _qkv(rng, B, Sq, Sk, Hq, Hkv, d, "bf16")
+    scale = 1 / math.sqrt(d)
+    o = torch.full((B, Sq, Hq, d), float("nan"), dtype=torch.float32, device=device())
+    lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=device())
+    ra.ring_attn_fwd_step(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16), o, lse,
+                          q_offset=q_off, kv_offset=kv_off, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    on, ln = to_np(o), to_np(lse)
+    assert np.all(np.isfinite(on))
+    group = Hq // Hkv
+    for h in (0, 17, 64, 127):
+        kh = h // group
+        o_ref, l_ref = oracle.attention_full(q[:, :, h:h + 1], k[:, :, kh:kh + 1], v[:, :, kh:kh + 1],
+                                             q_off + np.arange(Sq), kv_off + np.arange(Sk), scale, causal)
+        oh, lh = on[:, :, h:h + 1], ln[:, h:h + 1]
+        err_o = max_abs(oh, o_ref)
+        err_l = lse_close(lh, l_ref, 1e-3)
+        report("fwd_step_wide", case=case, head=h, o_err=err_o, lse_err=err_l, o_rel=rel_to_max(oh, o_ref))
+        assert err_o <= 2e-2
+        assert rel_to_max(oh, o_ref) <= 2e-2
+        dead = ~np.isfinite(l_ref)
+        assert np.all(oh[np.transpose(dead, (0, 2, 1))] == 0)
+
+
 def test_fwd_step_is_bitwise_repeatable():
     ra = lib()
     rng = np.random.default_rng(1)
