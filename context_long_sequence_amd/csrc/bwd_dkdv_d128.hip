@@ -91,6 +91,40 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   const int n_q = qt_end - qt_begin;
   const int n_iter = n_q * group;
 
+  // Tile order: first the tiles in which some element of some wave of the
+  // workgroup may be invisible (they run the masked body), then the rest (the
+  // unmasked body, no selects).  Per query head the masked tiles are a prefix
+  // [qt_begin, qt_begin + n_pre) (the causal diagonal: tiles whose first query
+  // precedes the workgroup's last key) and, when the shard ends inside a tile, the
+  // last tile.  A workgroup with keys past the chunk end, and every packed-row
+  // workgroup, runs all its tiles masked.
+  int n_pre = n_q, n_tail = 0;
+  if (!kSeg && k0 + 32 * NW <= a.Sk) {
+    int64_t diag_end = qt_begin;  // first tile whose first query follows the workgroup's last key
+    if (a.causal) {
+      const int64_t last_rel = a.kv_offset + k0 + 32 * NW - 1 - a.q_offset;  // last key, in query coordinates
+      diag_end = last_rel < 0 ? 0 : last_rel / QT + 1;
+    }
+    n_pre = (int)min<int64_t>(n_q, max<int64_t>(0, diag_end - qt_begin));
+    n_tail = (a.Sq % QT != 0 && qt_end - 1 >= qt_begin + n_pre) ? 1 : 0;
+  }
+  const int n_m = n_pre + n_tail;     // masked tiles per query head
+  const int n_u = n_q - n_m;          // unmasked tiles per query head
+  const int n_masked = n_m * group;   // sequence positions [0, n_masked) are masked
+  // Query head and tile of sequence position t.
+  auto tile_of = [&](int t, int& hq, int& qt) {
+    if (t < n_masked) {
+      const int h = t / n_m, r = t - h * n_m;
+      hq = g * group + h;
+      qt = r < n_pre ? qt_begin + r : qt_end - 1;
+    } else {
+      const int u = t - n_masked;
+      const int h = u / n_u;
+      hq = g * group + h;
+      qt = qt_begin + n_pre + (u - h * n_u);
+    }
+  };
+
   // Visibility of query q0 + 16*half + i to this lane's key: lo - q0 <= i < hi - q0
   // (causal rule and the end of the query shard; 32-bit: offsets clamped to +-2^30,
   // q0 <= 2^30).  A key past the chunk end sees nothing.
@@ -122,18 +156,17 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     coff[r] = (uint32_t)(row * q_rb + ((lane & 15) ^ swz(row)) * 16);
   }
   auto issue = [&](int t, __bf16* qs, __bf16* ds, float* xs) {
-    const int hq = g * group + t / n_q;
-    const int q0 = (qt_begin + t % n_q) * QT;
+    int hq, qt;
+    tile_of(t, hq, qt);
+    const int q0 = qt * QT;
     const int64_t hoff = (int64_t)q0 * q_rb + (int64_t)hq * (kD * 2);
     const int64_t bytes = (int64_t)(a.Sq - 1 - q0) * q_rb + kD * 2;
     const buffer_rsrc rq = make_rsrc(qg_base + hoff, bytes);
     const buffer_rsrc rd = make_rsrc(dg_base + hoff, bytes);
     char* dq_ = reinterpret_cast<char*>(qs) + 4 * wave * 1024;
     char* dd_ = reinterpret_cast<char*>(ds) + 4 * wave * 1024;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) buffer_load_lds16(rq, dq_ + r * 1024, coff[r]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) buffer_load_lds16(rd, dd_ + r * 1024, coff[r]);
+    // The per-query row first: wave 0 rescales its LSE row one step later and
+    // waits for this copy alone.
     const int64_t li = ((int64_t)b * a.Hq + hq) * a.Sq + q0;
     const void* src = a.lse + li;
     if (wave == 1) src = a.delta + li;
@@ -141,9 +174,26 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
       if (wave == 2) src = seg_row + a.q_offset + q0;
     }
     buffer_load_lds4(make_rsrc(src, (int64_t)(a.Sq - q0) * 4), xs + wave * QT, (uint32_t)lane * 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) buffer_load_lds16(rq, dq_ + r * 1024, coff[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) buffer_load_lds16(rd, dd_ + r * 1024, coff[r]);
   };
   constexpr int kCopiesPerTile = 9;
   static_assert(kCopiesPerTile == 2 * (QT / 4 / 4) + 1, "copy count per wave and tile");
+
+  // The LSE row of a tile is used as -LSE * log2(e) (the exponent of P in base 2).
+  // Wave 0, which copied it, rescales it in place one step before the tile is
+  // used: it reads the row at the start of step t (after waiting for its copy of
+  // tile t+1's row, which precedes the 8 row-block copies of that tile and the 9 of
+  // tile t+2) and writes it back after step t's arithmetic; the barrier of step t+1
+  // publishes it.  Saves 32 multiplications per lane and tile in the other waves.
+  auto rescale_wait = [&](bool next2) {
+    if (next2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(17));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+  };
 
   // LDS operand offsets.  Q and dO rows (A of S = Q K^T, dP = dO V^T): row
   // 32*qb + key_of_row(col), 16-byte chunk 2c+half, i.e. 8192*qb + (rA ^ (c << 5)).
@@ -158,27 +208,32 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
   };
 
-  // One 64-query tile against the wave's 32 keys, as two 32-query blocks in one
-  // straight-line body: the scores of both blocks first, then per block the
-  // softmax and the dV/dK products, so the scheduler can overlap one block's vector
-  // work with the other block's MFMAs.  P uses the final LSE as is: a query whose
-  // LSE is -inf sees no key at all, so its elements are masked in every block that
-  // holds it.  The bounds mask is applied to every block (it also zeroes blocks
-  // that lie entirely before the wave's keys); the segment test only where needed.
   // One 64-query tile = two 32-query blocks against the wave's 32 keys.  Per block:
   // score MFMAs (S = Q K^T, dP = dO V^T; lane = key, register i of half h = query
   // q0 + 16h + i), per element P = exp(S - LSE) and dS = P (dP - delta) on the
   // vector ALU, then gradient MFMAs (dV += P^T dO, dK += dS^T Q).  With one wave per
-  // SIMD the two units only work side by side if the instruction stream interleaves
-  // them, so the tile is laid out as a pipeline pinned with scheduling fences:
+  // SIMD the vector ALU only runs beside the matrix unit if the instruction stream
+  // interleaves them and the vector instructions between two MFMAs do not depend on
+  // one another, so the tile is one straight-line body of 64 MFMA slots pinned with
+  // scheduling fences, and each element passes through four stages in four
+  // consecutive slots (A: copy S and dP out of the accumulation registers; B: the
+  // exponent S*scale*log2(e) - LSE*log2(e), dP - delta and, in the masked body, the
+  // mask; C: exp2; D: dS = P * (dP - delta)):
   //   P1: block 0 scores                  | block 1 operand reads
-  //   P2: block 1 scores                  | block 0 elements, block 0 dO^T/Q^T reads
-  //   P3: block 0 gradients               | block 1 elements, block 1 dO^T/Q^T reads
-  //   P4: block 1 gradients
-  // Each MFMA slot (32 clocks) carries at most one element.  P uses the final LSE as
-  // is: a query whose LSE is -inf sees no key at all, so the element mask zeroes it.
-  auto compute = [&](int it, const __bf16* qt_, const __bf16* dt_, const float* xs) {
-    const int qtile0 = (qt_begin + it % n_q) * QT;
+  //   P2: block 1 scores                  | block 0 elements, dO^T/Q^T reads
+  //   P3: block 0 gradients               | block 1 elements (and block 0's last 3)
+  //   P4: block 1 gradients               | block 1's last 3 elements
+  // A slot then holds at most six independent vector instructions besides its MFMA.
+  // The masked body (kMask) sets the exponent of every invisible element to -inf, so
+  // P and dS are exactly 0 there: the causal rule, the ends of the query shard and
+  // of the chunk and, for packed rows, the segment test.  P uses the final LSE as
+  // is: a query whose LSE is -inf sees no key at all, so it only occurs in masked
+  // tiles, where its elements are invisible.
+  auto compute = [&](auto mask_tag, int it, const __bf16* qt_, const __bf16* dt_, const float* xs) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    int hq_unused, qt_cur;
+    tile_of(it, hq_unused, qt_cur);
+    const int qtile0 = qt_cur * QT;
     const char* qc = reinterpret_cast<const char*>(qt_);
     const char* dc = reinterpret_cast<const char*>(dt_);
     f32x16 s[2], dp[2];
@@ -186,6 +241,9 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     bf16x8 dot[2][2][4], qtf[2][2][4];    // [qb][m][db]: dO^T and Q^T operands
     bf16x8 pf[2][2], sf[2][2];            // [qb][m]: packed P and dS, elements 8m..8m+7
     float lq[2][16], dl[2][16];           // -LSE*log2(e) and delta of the block's queries
+    int sgq[2][16];                       // segment ids of the block's queries (packed rows)
+    float ea[2][16], eb[2][16];           // element pipeline registers
+    float pe[2][16], de[2][16];           // P and dS
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
     auto read_op = [&](int qb, int c) {
       fq[qb][c] = load_bf16x8(qc + 8192 * qb + (rA ^ (c << 5)));
@@ -194,8 +252,9 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     auto read_rows = [&](int qb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        lq[qb][i] = xs[32 * qb + 16 * half + i] * -kLog2e;
+        lq[qb][i] = xs[32 * qb + 16 * half + i];
         dl[qb][i] = xs[QT + 32 * qb + 16 * half + i];
+        if constexpr (kMask && kSeg) sgq[qb][i] = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 16 * half + i]);
       }
     };
     auto read_tr = [&](int qb, int m, int db) {
@@ -206,60 +265,58 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
       dot[qb][m][db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
       qtf[qb][m][db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
     };
-    float pe[2][16], de[2][16];
-    auto element = [&](int qb, int i) {
-      float pv = exp2_fast(__builtin_fmaf(s[qb][i], a.scale_log2, lq[qb][i]));
-      float dv_ = pv * (dp[qb][i] - dl[qb][i]);
-      // The empty statement is ordered with the fences, so the element cannot sink
-      // towards its later use.
-      asm volatile("" : "+v"(pv), "+v"(dv_));
-      pe[qb][i] = pv;
-      de[qb][i] = dv_;
+    // Element stages; the empty statements keep each stage's results in its slot.
+    auto stage_a = [&](int qb, int i) {
+      float x = s[qb][i], y = dp[qb][i];
+      asm volatile("" : "+v"(x), "+v"(y));
+      ea[qb][i] = x;
+      eb[qb][i] = y;
     };
-    // Element mask, applied after a block's elements and only where the block is not
-    // entirely visible (wave-uniform test): the causal rule, the ends of the query
-    // shard and of the chunk, and (packed rows) the segment test.  Selects, so an
-    // infinite P of an invisible element never reaches dV or dK.
-    auto mask_and_pack = [&](int qb) {
-      const int q0 = qtile0 + 32 * qb;
-      bool partial = (q0 + 32 > a.Sq) || (kw + 32 > a.Sk);
-      if (a.causal) partial |= (a.kv_offset + kw + 31 > a.q_offset + q0);
-      if (partial) {
-        const int lo = vis_lo - q0, hi = vis_hi - q0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const bool vis = (i >= lo) & (i < hi);
-          pe[qb][i] = vis ? pe[qb][i] : 0.0f;
-          de[qb][i] = vis ? de[qb][i] : 0.0f;
-        }
+    auto stage_b = [&](int qb, int i) {
+      float x = __builtin_fmaf(ea[qb][i], a.scale_log2, lq[qb][i]);
+      float y = eb[qb][i] - dl[qb][i];
+      if constexpr (kMask) {
+        const int q0 = qtile0 + 32 * qb;
+        bool vis = (i >= vis_lo - q0) & (i < vis_hi - q0);
+        if constexpr (kSeg) vis &= sgq[qb][i] == seg_k;
+        x = vis ? x : -__builtin_inff();
       }
-      if constexpr (kSeg) {
-        // Segment ids are nondecreasing: only blocks that straddle a segment boundary
-        // need the per-element segment test.
-        const int sq_lo = __builtin_bit_cast(int, xs[2 * QT + 32 * qb]);
-        const int sq_hi = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 31]);
-        if (!(sq_lo == sq_hi && sq_lo == seg_w_lo && seg_w_lo == seg_w_hi)) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const bool ok = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 16 * half + i]) == seg_k;
-            pe[qb][i] = ok ? pe[qb][i] : 0.0f;
-            de[qb][i] = ok ? de[qb][i] : 0.0f;
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const float* pp = &pe[qb][8 * m];
-        const float* dd = &de[qb][8 * m];
-        pf[qb][m] = to_bf16x8(pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]);
-        sf[qb][m] = to_bf16x8(dd[0], dd[1], dd[2], dd[3], dd[4], dd[5], dd[6], dd[7]);
-      }
+      asm volatile("" : "+v"(x), "+v"(y));
+      ea[qb][i] = x;
+      eb[qb][i] = y;
+    };
+    auto stage_c = [&](int qb, int i) {
+      float x = exp2_fast(ea[qb][i]);
+      asm volatile("" : "+v"(x));
+      pe[qb][i] = x;
+    };
+    auto stage_d = [&](int qb, int i) {
+      float y = pe[qb][i] * eb[qb][i];
+      asm volatile("" : "+v"(y));
+      de[qb][i] = y;
+    };
+    // The stages of block qb that fall in its k-th element slot (k = 0 .. 18).
+    auto elements = [&](int qb, int k) {
+      if (k >= 3 && k < 19) stage_d(qb, k - 3);
+      if (k >= 2 && k < 18) stage_c(qb, k - 2);
+      if (k >= 1 && k < 17) stage_b(qb, k - 1);
+      if (k < 16) stage_a(qb, k);
+    };
+    // bf16 packing of elements 8m + 2j, 8m + 2j + 1 (j = 0 .. 3) of P and dS.
+    auto pack = [&](int qb, int m, int j) {
+      const f32x2 p2 = {pe[qb][8 * m + 2 * j], pe[qb][8 * m + 2 * j + 1]};
+      const f32x2 d2 = {de[qb][8 * m + 2 * j], de[qb][8 * m + 2 * j + 1]};
+      const bf16x2 pb = __builtin_convertvector(p2, bf16x2);
+      const bf16x2 db2 = __builtin_convertvector(d2, bf16x2);
+      pf[qb][m][2 * j] = pb[0];
+      pf[qb][m][2 * j + 1] = pb[1];
+      sf[qb][m][2 * j] = db2[0];
+      sf[qb][m][2 * j + 1] = db2[1];
     };
 
     // P1: block 0 scores; block 1 operand reads in their shadow.
 #pragma unroll
     for (int c = 0; c < 8; ++c) read_op(0, c);
-    read_rows(0);
     fence();
     s[0] = f32x16{};
     dp[0] = f32x16{};
@@ -267,6 +324,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     for (int c = 0; c < 8; ++c) {
       s[0] = mfma_bf16(fq[0][c], kf[c], s[0]);
       fq[1][c] = load_bf16x8(qc + 8192 + (rA ^ (c << 5)));
+      if (c == 2) read_rows(0);
       fence();
       dp[0] = mfma_bf16(fd[0][c], vf[c], dp[0]);
       fd[1][c] = load_bf16x8(dc + 8192 + (rA ^ (c << 5)));
@@ -274,50 +332,53 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     }
     read_rows(1);
     fence();
-    // P2: block 1 scores; block 0 elements and its m = 0 transposed reads.
+    // P2: block 1 scores; block 0 elements 0..15 (stages up to slot 15), its m = 0
+    // transposed operands, and the packing of its elements 0..7.
     s[1] = f32x16{};
     dp[1] = f32x16{};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      s[1] = mfma_bf16(fq[1][c], kf[c], s[1]);
-      element(0, 2 * c);
-      if (c < 4) read_tr(0, 0, c);
-      fence();
-      dp[1] = mfma_bf16(fd[1][c], vf[c], dp[1]);
-      element(0, 2 * c + 1);
+    for (int k = 0; k < 16; ++k) {
+      if (k % 2 == 0)
+        s[1] = mfma_bf16(fq[1][k / 2], kf[k / 2], s[1]);
+      else
+        dp[1] = mfma_bf16(fd[1][k / 2], vf[k / 2], dp[1]);
+      elements(0, k);
+      if (k < 4) read_tr(0, 0, k);
+      if (k >= 11 && k < 15) pack(0, 0, k - 11);
       fence();
     }
-    mask_and_pack(0);
-    fence();
-    // P3: block 0 gradients; block 1 elements and the remaining transposed reads.
+    // P3: block 0 gradients (slot 2(4m + db): dV, slot +1: dK); block 0's last
+    // stages, block 1 elements, the packing of block 0's elements 8..15 and of block
+    // 1's elements 0..7; the remaining transposed operands of block 0 (m = 1) and
+    // block 1's m = 0.
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
+    for (int k = 0; k < 16; ++k) {
+      const int m = k / 8, db = (k / 2) % 4;
+      if (k % 2 == 0)
         dv[db] = mfma_bf16(pf[0][m], dot[0][m][db], dv[db]);
-        element(1, 8 * m + 2 * db);
-        if (m == 0) read_tr(0, 1, db);
-        fence();
+      else
         dk[db] = mfma_bf16(sf[0][m], qtf[0][m][db], dk[db]);
-        element(1, 8 * m + 2 * db + 1);
-        if (m == 1) read_tr(1, 0, db);
-        fence();
-      }
-    mask_and_pack(1);
-    fence();
-    // P4: block 1 gradients; its m = 1 transposed reads in the shadow of m = 0.
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      dv[db] = mfma_bf16(pf[1][0], dot[1][0][db], dv[db]);
-      read_tr(1, 1, db);
-      fence();
-      dk[db] = mfma_bf16(sf[1][0], qtf[1][0][db], dk[db]);
+      if (k < 3) elements(0, 16 + k);
+      elements(1, k);
+      if (k >= 3 && k < 7) pack(0, 1, k - 3);
+      if (k >= 11 && k < 15) pack(1, 0, k - 11);
+      if (k < 8 && k % 2 == 0) read_tr(0, 1, db);
+      if (k >= 8 && k % 2 == 1) read_tr(1, 0, db);
       fence();
     }
+    // P4: block 1 gradients; block 1's last stages, the packing of its elements
+    // 8..15 and its m = 1 transposed operands.
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      dv[db] = mfma_bf16(pf[1][1], dot[1][1][db], dv[db]);
-      dk[db] = mfma_bf16(sf[1][1], qtf[1][1][db], dk[db]);
+    for (int k = 0; k < 16; ++k) {
+      const int m = k / 8, db = (k / 2) % 4;
+      if (k % 2 == 0)
+        dv[db] = mfma_bf16(pf[1][m], dot[1][m][db], dv[db]);
+      else
+        dk[db] = mfma_bf16(sf[1][m], qtf[1][m][db], dk[db]);
+      if (k < 3) elements(1, 16 + k);
+      if (k >= 3 && k < 7) pack(1, 1, k - 3);
+      if (k < 8 && k % 2 == 0) read_tr(1, 1, db);
+      fence();
     }
   };
 
@@ -327,24 +388,50 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   // copies still in flight.  The empty asm statements keep the compiler from
   // moving LDS accesses across it; the copies of this wave are waited for
   // explicitly (vmcnt counts them in issue order).
-  auto step = [&](int it, const __bf16* qc, const __bf16* dc, const float* xc, __bf16* qn, __bf16* dn, float* xn) {
+  auto step = [&](auto mask_tag, int it, const __bf16* qc, const __bf16* dc, const float* xc, float* x1,
+                  __bf16* qn, __bf16* dn, float* xn) {
+    asm volatile("" ::: "memory");
     if (it + 1 < n_iter)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesPerTile);  // vmcnt(9): tile it+1 may stay in flight
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerTile));  // tile it+1 may stay in flight
     else
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (it + 2 < n_iter) issue(it + 2, qn, dn, xn);
-    compute(it, qc, dc, xc);
+    const bool resc = wave == 0 && it + 1 < n_iter;
+    float lraw = 0.0f;
+    if (resc) {
+      rescale_wait(it + 2 < n_iter);
+      lraw = x1[lane];
+    }
+    compute(mask_tag, it, qc, dc, xc);
+    if (resc) {
+      asm volatile("" : "+v"(lraw));  // keeps the multiplication (and the wait for the read) here
+      x1[lane] = lraw * -kLog2e;
+    }
   };
 
   if (n_iter > 0) issue(0, qs0, ds0, xs0);
   if (n_iter > 1) issue(1, qs1, ds1, xs1);
-  for (int it = 0; it < n_iter; it += 3) {
-    step(it, qs0, ds0, xs0, qs2, ds2, xs2);
-    if (it + 1 < n_iter) step(it + 1, qs1, ds1, xs1, qs0, ds0, xs0);
-    if (it + 2 < n_iter) step(it + 2, qs2, ds2, xs2, qs1, ds1, xs1);
+  if (wave == 0 && n_iter > 0) {
+    rescale_wait(n_iter > 1);
+    xs0[lane] = xs0[lane] * -kLog2e;
+  }
+  // Masked tiles first, in whole groups of three (a group that reaches into the
+  // unmasked tiles runs masked: correct, only slower), so that both loops start at
+  // slot 0 of the ring.
+  const int n_masked3 = min(n_iter, (n_masked + 2) / 3 * 3);
+  int it = 0;
+  for (; it < n_masked3; it += 3) {
+    step(BoolTag<true>{}, it, qs0, ds0, xs0, xs1, qs2, ds2, xs2);
+    if (it + 1 < n_iter) step(BoolTag<true>{}, it + 1, qs1, ds1, xs1, xs2, qs0, ds0, xs0);
+    if (it + 2 < n_iter) step(BoolTag<true>{}, it + 2, qs2, ds2, xs2, xs0, qs1, ds1, xs1);
+  }
+  for (; it < n_iter; it += 3) {
+    step(BoolTag<false>{}, it, qs0, ds0, xs0, xs1, qs2, ds2, xs2);
+    if (it + 1 < n_iter) step(BoolTag<false>{}, it + 1, qs1, ds1, xs1, xs2, qs0, ds0, xs0);
+    if (it + 2 < n_iter) step(BoolTag<false>{}, it + 2, qs2, ds2, xs2, xs0, qs1, ds1, xs1);
   }
 
   // lane = d column, register i of half h = key kw + mfma32_row(i, h).

@@ -220,9 +220,9 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
   // statements keep the compiler from moving LDS accesses across it.
   auto step = [&](int t, const __bf16* kc, const __bf16* vc, __bf16* kn, __bf16* vn) {
     if (t + 1 < kt_end)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesPerTile);  // tile t+1 may stay in flight
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopiesPerTile));  // tile t+1 may stay in flight
     else
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");

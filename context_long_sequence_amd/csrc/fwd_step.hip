@@ -597,11 +597,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
   f32x16 s_next = f32x16{};
   auto step = [&](int t, const __bf16* kq, const __bf16* vc, __bf16* kn, __bf16* vn) {
     if (t + 2 < kt_end)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kCopiesPerTile));  // both tensors of the last step in flight
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopiesPerTile));  // both tensors of the last step in flight
     else if (t + 1 < kt_end)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kCopiesPerTile);  // its V copies in flight
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopiesPerTile));  // its V copies in flight
     else
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -622,7 +622,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
       copy_tile(vbase, t + 1, vs1);
     }
     if (t + 2 < kt_end) copy_tile(kbase, t + 2, ks2);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");

@@ -170,6 +170,12 @@ __device__ __forceinline__ void buffer_load_lds16(buffer_rsrc rs, void* dst, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, voffset, 0, 0, 0);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8).  waitcnt_vm(n): at most n vector-memory operations outstanding;
+// waitcnt_vm_lgkm0(n): the same and no LDS operation outstanding.
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int waitcnt_vm_lgkm0(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14); }
+
 // Workgroup -> XCD remap.  Consecutive workgroup ids are dispatched round-robin
 // over the 8 XCDs of an MI355X; this returns a logical id such that each XCD
 // receives one contiguous range of logical ids (so workgroups that share K/V
