@@ -111,19 +111,27 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   const int n_m = n_pre + n_tail;     // masked tiles per query head
   const int n_u = n_q - n_m;          // unmasked tiles per query head
   const int n_masked = n_m * group;   // sequence positions [0, n_masked) are masked
-  // Query head and tile of sequence position t.
-  auto tile_of = [&](int t, int& hq, int& qt) {
-    if (t < n_masked) {
-      const int h = t / n_m, r = t - h * n_m;
-      hq = g * group + h;
-      qt = r < n_pre ? qt_begin + r : qt_end - 1;
-    } else {
-      const int u = t - n_masked;
-      const int h = u / n_u;
-      hq = g * group + h;
-      qt = qt_begin + n_pre + (u - h * n_u);
+  // Walk over that order.  The copies and the tile bodies each visit the tiles in
+  // order, so each keeps a walker (query head within the group, position within
+  // the head's run of masked or unmasked tiles) instead of dividing per tile.
+  struct TileWalk {
+    int h, r;
+    bool masked;
+  };
+  auto walk_tile = [&](const TileWalk& w, int& hq, int& qt) {
+    hq = g * group + w.h;
+    qt = w.masked ? (w.r < n_pre ? qt_begin + w.r : qt_end - 1) : qt_begin + n_pre + w.r;
+  };
+  auto walk_next = [&](TileWalk& w) {
+    if (++w.r == (w.masked ? n_m : n_u)) {
+      w.r = 0;
+      if (++w.h == group) {
+        w.h = 0;
+        w.masked = false;
+      }
     }
   };
+  TileWalk issue_walk{0, 0, n_m > 0}, compute_walk{0, 0, n_m > 0};
 
   // Visibility of query q0 + 16*half + i to this lane's key: lo - q0 <= i < hi - q0
   // (causal rule and the end of the query shard; 32-bit: offsets clamped to +-2^30,
@@ -155,14 +163,16 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     const int row = (4 * wave + r) * 4 + (lane >> 4);
     coff[r] = (uint32_t)(row * q_rb + ((lane & 15) ^ swz(row)) * 16);
   }
-  auto issue = [&](int t, __bf16* qs, __bf16* ds, float* xs) {
+  auto issue = [&](__bf16* qs, __bf16* ds, float* xs) {
     int hq, qt;
-    tile_of(t, hq, qt);
+    walk_tile(issue_walk, hq, qt);
+    walk_next(issue_walk);
     const int q0 = qt * QT;
+    const int rows = min(a.Sq - q0, QT);  // >= 1; the descriptors end at the tile's last valid row
     const int64_t hoff = (int64_t)q0 * q_rb + (int64_t)hq * (kD * 2);
-    const int64_t bytes = (int64_t)(a.Sq - 1 - q0) * q_rb + kD * 2;
-    const buffer_rsrc rq = make_rsrc(qg_base + hoff, bytes);
-    const buffer_rsrc rd = make_rsrc(dg_base + hoff, bytes);
+    const int bytes = (rows - 1) * q_rb + kD * 2;  // < 2^31: q_rb <= 4096 * 256
+    const buffer_rsrc rq = make_rsrc32(qg_base + hoff, bytes);
+    const buffer_rsrc rd = make_rsrc32(dg_base + hoff, bytes);
     char* dq_ = reinterpret_cast<char*>(qs) + 4 * wave * 1024;
     char* dd_ = reinterpret_cast<char*>(ds) + 4 * wave * 1024;
     // The per-query row first: wave 0 rescales its LSE row one step later and
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     if constexpr (kSeg) {
       if (wave == 2) src = seg_row + a.q_offset + q0;
     }
-    buffer_load_lds4(make_rsrc(src, (int64_t)(a.Sq - q0) * 4), xs + wave * QT, (uint32_t)lane * 4);
+    buffer_load_lds4(make_rsrc32(src, rows * 4), xs + wave * QT, (uint32_t)lane * 4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) buffer_load_lds16(rq, dq_ + r * 1024, coff[r]);
 #pragma unroll
@@ -232,7 +242,8 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   auto compute = [&](auto mask_tag, int it, const __bf16* qt_, const __bf16* dt_, const float* xs) {
     constexpr bool kMask = decltype(mask_tag)::value;
     int hq_unused, qt_cur;
-    tile_of(it, hq_unused, qt_cur);
+    walk_tile(compute_walk, hq_unused, qt_cur);
+    walk_next(compute_walk);
     const int qtile0 = qt_cur * QT;
     const char* qc = reinterpret_cast<const char*>(qt_);
     const char* dc = reinterpret_cast<const char*>(dt_);
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (it + 2 < n_iter) issue(it + 2, qn, dn, xn);
+    if (it + 2 < n_iter) issue(qn, dn, xn);
     const bool resc = wave == 0 && it + 1 < n_iter;
     float lraw = 0.0f;
     if (resc) {
@@ -412,8 +423,8 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     }
   };
 
-  if (n_iter > 0) issue(0, qs0, ds0, xs0);
-  if (n_iter > 1) issue(1, qs1, ds1, xs1);
+  if (n_iter > 0) issue(qs0, ds0, xs0);
+  if (n_iter > 1) issue(qs1, ds1, xs1);
   if (wave == 0 && n_iter > 0) {
     rescale_wait(n_iter > 1);
     xs0[lane] = xs0[lane] * -kLog2e;
@@ -434,18 +445,36 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     if (it + 2 < n_iter) step(BoolTag<false>{}, it + 2, qs2, ds2, xs2, xs0, qs1, ds1, xs1);
   }
 
-  // lane = d column, register i of half h = key kw + mfma32_row(i, h).
+  // lane = d column, register i of half h = key kw + mfma32_row(i, h).  The
+  // read-modify-write of dK and dV goes in groups of 16 keys x 2 tensors so that the
+  // loads of a group are in flight together (the two pointers do not alias).
+  float* __restrict__ dkp = a.dk;
+  float* __restrict__ dvp = a.dv;
+  const float ks = a.scale;
+  const int64_t base = ((int64_t)b * a.Sk + kw) * kv_rs + (int64_t)g * kD + col;
+  const bool full = kw + 32 <= a.Sk;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db) {
+    float ok[16], ov[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = kw + mfma32_row(i, half);
-      if (key < a.Sk) {
-        const int64_t off = ((int64_t)b * a.Sk + key) * kv_rs + (int64_t)g * kD + 32 * db + col;
-        a.dk[off] += a.scale * dk[db][i];
-        a.dv[off] += dv[db][i];
+      const int r = mfma32_row(i, half);
+      const int64_t off = base + (int64_t)r * kv_rs + 32 * db;
+      if (full || kw + r < a.Sk) {
+        ok[i] = dkp[off];
+        ov[i] = dvp[off];
       }
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = mfma32_row(i, half);
+      const int64_t off = base + (int64_t)r * kv_rs + 32 * db;
+      if (full || kw + r < a.Sk) {
+        dkp[off] = ok[i] + ks * dk[db][i];
+        dvp[off] = ov[i] + dv[db][i];
+      }
+    }
+  }
 }
 
 }  // namespace

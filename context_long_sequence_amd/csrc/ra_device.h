@@ -161,6 +161,10 @@ __device__ __forceinline__ buffer_rsrc make_rsrc(const void* base, int64_t bytes
   const int n = (int)(bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes));
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
+// The same for a range known to lie in [0, 2^31).
+__device__ __forceinline__ buffer_rsrc make_rsrc32(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
 // 4 bytes per lane from base + voffset into LDS at dst + 4*lane (dst wave-uniform).
 __device__ __forceinline__ void buffer_load_lds4(buffer_rsrc rs, void* dst, uint32_t voffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 4, voffset, 0, 0, 0);
