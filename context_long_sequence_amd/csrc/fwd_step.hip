@@ -546,9 +546,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
       }
     }
 
-    float r = sc[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) r = fmaxf(r, sc[i]);
+    // Row max and (below) row sum as trees of independent operations, so that the
+    // vector instructions between two MFMAs do not wait on one another.
+    auto max3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
+    const float r = fmaxf(max3(max3(sc[0], sc[1], sc[2]), max3(sc[3], sc[4], sc[5]), max3(sc[6], sc[7], sc[8])),
+                          max3(max3(sc[9], sc[10], sc[11]), max3(sc[12], sc[13], sc[14]), sc[15]));
     const float tmax = half_max(r) * a.scale_log2;
     // Lazy rescaling: the running max only moves when a row's max grows by more
     // than kSlack (log2 units), so P stays <= 2^kSlack and most tiles skip the
@@ -563,13 +565,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
     }
     const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
     float p[16];
-    float psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[i] = exp2_fast(__builtin_fmaf(sc[i], a.scale_log2, neg_m));
-      psum += p[i];
-    }
-    l_run += psum;
+    for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(sc[i], a.scale_log2, neg_m));
+    float ps4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ps4[j] = (p[4 * j] + p[4 * j + 1]) + (p[4 * j + 2] + p[4 * j + 3]);
+    l_run += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
     const bf16x8 pf0 = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
     const bf16x8 pf1 = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
 
