@@ -184,15 +184,19 @@ def main():
     torch.cuda.synchronize()
     workspace_peak = torch.cuda.max_memory_allocated() - base_alloc
 
-    # Timed region: K whole steps.
+    # Timed region: K whole steps (events around each step give the median as well).
     timer = Timer(torch)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         step(timer)
+        marks[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
 
     flops = {"all": f_fwd + f_bwd, "fwd": f_fwd, "bwd": f_bwd}[args.only]
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -231,7 +235,9 @@ def main():
         "live_pairs": pairs,
         "algorithmic_flop": {"fwd": f_fwd, "bwd": f_bwd},
         "per_step_ms": {k: round(v, 4) for k, v in per_step_ms.items()},
-        "timer_ms": {"host_wall_per_step": round(ms_per_step, 4)},
+        "timer_ms": {"host_wall_per_step": round(ms_per_step, 4),
+                     "event_median_per_step": round(float(np.median(step_ms)), 4),
+                     "event_min_per_step": round(min(step_ms), 4)},
     }
     if t_fwd_step and t_merge and args.only in ("fwd", "all"):
         fwd_ms = per_step_ms["fwd_step"] + per_step_ms.get("merge", 0.0)
@@ -249,6 +255,22 @@ def main():
                           "score_matrix_avoided_bytes": C * cfg.S * cfg.Hq * 4}
 
     if not args.no_extras:
+        # Cold caches: before each of 3 steps, 1 GiB is written (more than the 4 MiB L2
+        # per XCD and the 256 MiB Infinity Cache), then the step is timed alone.
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold = []
+        for _ in range(3):
+            flush.fill_(1.0)
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record()
+            step()
+            b_ev.record()
+            torch.cuda.synchronize()
+            cold.append(a_ev.elapsed_time(b_ev))
+        del flush
+        cold_ms = float(np.median(cold))
+        extra["cache_flushed"] = {"ms_per_step_median": round(cold_ms, 4),
+                                  "tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2), "steps": len(cold)}
         extra.update(side_measurements(torch, ra, np, dev, CONFIGS, make_workload))
         zz = extra["zigzag_64k_cp8"]
         # the ring runs at the pace of its slowest rank: contiguous rank 7 (this line's
@@ -528,15 +550,19 @@ def cpu_baseline(cfg, wl=None):
     import oracle
     from synthetic import make_workload
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in infos] or [1])
+        if infos:
+            blas = f"{infos[0].get('internal_api', '?')} {infos[0].get('version', '')}".strip()
     except Exception:  # noqa: BLE001
         threads = 1
     if wl is None:
         wl = make_workload(cfg, q_chunks=[cfg.rank])
     C, r = cfg.C, cfg.rank
-    R = 128
+    R = 512
     rows = np.arange(C - R, C)
     q_rows = wl.q_local[:, rows]
     do_rows = wl.do[:, rows]
@@ -553,7 +579,7 @@ def cpu_baseline(cfg, wl=None):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 numpy oracle fwd+bwd of the last {R} query rows of the 64K share "
                       f"(rank 7, all {cfg.Hq} heads, {cfg.S} keys each): {pairs} live pairs, "
-                      f"{flops:.3e} algorithmic flop in {dt:.1f} s"}
+                      f"{flops:.3e} algorithmic flop in {dt:.1f} s; numpy BLAS: {blas}"}
 
 
 if __name__ == "__main__":
