@@ -107,6 +107,11 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
   else if (a.causal)
     lim_base = (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, qg - a.kv_offset - 16 * half));
 
+  // The last chunk key the wave's first query sees (same clamp): tiles past it
+  // need the element mask.
+  const int wave_last_visible =
+      (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, a.q_offset + qw - a.kv_offset));
+
   f32x16 dq[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
@@ -123,9 +128,10 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
   }
   auto issue = [&](int t, __bf16* kdst, __bf16* vdst) {
     const int k0 = t * kTile;
-    const int64_t bytes = (int64_t)(a.Sk - 1 - k0) * kv_rb + kD * 2;
-    const buffer_rsrc rk = make_rsrc(kbase + (int64_t)k0 * kv_rb, bytes);
-    const buffer_rsrc rv = make_rsrc(vbase + (int64_t)k0 * kv_rb, bytes);
+    // Through the tile's last valid key row; < 2^31 since kv_rb <= 4096 * 256.
+    const int bytes = (min(a.Sk - k0, kTile) - 1) * kv_rb + kD * 2;
+    const buffer_rsrc rk = make_rsrc32(kbase + (int64_t)k0 * kv_rb, bytes);
+    const buffer_rsrc rv = make_rsrc32(vbase + (int64_t)k0 * kv_rb, bytes);
     char* dk = reinterpret_cast<char*>(kdst) + kDqBlocks * wave * 1024;
     char* dv = reinterpret_cast<char*>(vdst) + kDqBlocks * wave * 1024;
 #pragma unroll
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
   auto compute = [&](int t, const __bf16* kt_, const __bf16* vt_) {
       const int k0 = t * kTile;
       bool partial = (k0 + kTile > a.Sk) || (qw + 32 > a.Sq);  // wave-uniform
-      if (a.causal) partial |= (a.kv_offset + k0 + kTile - 1 > a.q_offset + qw);
+      if (a.causal) partial |= (k0 + kTile - 1 > wave_last_visible);
       if constexpr (kSeg) {
         // Segment ids are nondecreasing: only blocks that straddle a segment
         // boundary need the per-element segment test.

@@ -461,6 +461,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
 
   // Causal limit: key k0 + 16*half + i is visible iff i <= causal_lim - k0.  Clamped
   // to +-2^30 (k0 <= 2^30), which keeps the test exact without 64-bit arithmetic.
+  // wave_last_visible: the last chunk key the wave's first query sees (same clamp).
+  const int wave_last_visible =
+      (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, a.q_offset + qw - a.kv_offset));
   int causal_lim = 1 << 30;
   if (a.causal) {
     const int64_t c = a.q_offset + qi - a.kv_offset - 16 * half;
@@ -479,8 +482,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
   }
   auto copy_tile = [&](const char* base, int t, __bf16* dst) {
     const int k0 = t * BN;
-    const int64_t bytes = (int64_t)(a.Sk - 1 - k0) * kv_rb + D * 2;  // through the last key's row
-    const buffer_rsrc rs = make_rsrc(base + (int64_t)k0 * kv_rb, bytes);
+    // Through the tile's last valid key row; < 2^31 since kv_rb <= 4096 * 256.
+    const int bytes = (min(a.Sk - k0, BN) - 1) * kv_rb + D * 2;
+    const buffer_rsrc rs = make_rsrc32(base + (int64_t)k0 * kv_rb, bytes);
     char* d = reinterpret_cast<char*>(dst) + kD128Blocks * wave * 1024;
 #pragma unroll
     for (int r = 0; r < kD128Blocks; ++r) buffer_load_lds16(rs, d + r * 1024, coff[r]);
@@ -520,7 +524,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
   auto consume = [&](f32x16 sc, const __bf16* vt, int t) {
     const int k0 = t * BN;
     bool partial = (k0 + BN > a.Sk);
-    if (a.causal) partial |= (a.kv_offset + k0 + BN - 1 > a.q_offset + qw);
+    if (a.causal) partial |= (k0 + BN - 1 > wave_last_visible);
     if constexpr (kSeg) {
       // Segment ids are nondecreasing: the block needs the segment test only if the
       // wave's queries and the tile's keys are not all in one and the same segment.
