@@ -599,9 +599,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
   // published with a bare s_barrier (a workgroup fence would also drain the copies
   // in flight; the empty asm statements keep LDS accesses on their side of it).
   // The slots freed by that barrier receive K(t+3) and V(t+2).
+  // `steady`: the caller guarantees t + 3 < kt_end, so the waits and copies need no
+  // tests (the bulk of the loop); the last steps go through the general form.
   f32x16 s_next = f32x16{};
-  auto step = [&](int t, const __bf16* kq, const __bf16* vc, __bf16* kn, __bf16* vn) {
-    if (t + 2 < kt_end)
+  auto step = [&](auto steady_tag, int t, const __bf16* kq, const __bf16* vc, __bf16* kn, __bf16* vn) {
+    constexpr bool kSteady = decltype(steady_tag)::value;
+    if (kSteady || t + 2 < kt_end)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopiesPerTile));  // both tensors of the last step in flight
     else if (t + 1 < kt_end)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopiesPerTile));  // its V copies in flight
@@ -610,8 +613,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (t + 3 < kt_end) copy_tile(kbase, t + 3, kn);
-    if (t + 2 < kt_end) copy_tile(vbase, t + 2, vn);
+    if (kSteady || t + 3 < kt_end) copy_tile(kbase, t + 3, kn);
+    if (kSteady || t + 2 < kt_end) copy_tile(vbase, t + 2, vn);
     // Scores of tile t+1 (on the last step the slot is stale and the result unused).
     const f32x16 sc = s_next;
     s_next = qk(kq);
@@ -636,19 +639,33 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
   // Slots: K(j) in ks[(j - kt_begin) % 3], V(j) in vs[(j - kt_begin) % 3].  Six
   // steps per iteration, so the two score register sets alternate without copies;
   // every exit leaves through a break, so only O, m and l are live there.
+  // The steady loop runs while all six of its steps have t + 3 < kt_end; the rest
+  // (at most 8 steps) runs through the general steps, which continue the same slot
+  // rotation (both loops advance t by 6).
   if (kt_begin < kt_end) {
-    for (int t = kt_begin;; t += 6) {
-      step(t, ks1, vs0, ks0, vs2);
+    const BoolTag<true> st;
+    const BoolTag<false> gen;
+    int t = kt_begin;
+    for (; t + 8 < kt_end; t += 6) {
+      step(st, t, ks1, vs0, ks0, vs2);
+      step(st, t + 1, ks2, vs1, ks1, vs0);
+      step(st, t + 2, ks0, vs2, ks2, vs1);
+      step(st, t + 3, ks1, vs0, ks0, vs2);
+      step(st, t + 4, ks2, vs1, ks1, vs0);
+      step(st, t + 5, ks0, vs2, ks2, vs1);
+    }
+    for (;; t += 6) {
+      step(gen, t, ks1, vs0, ks0, vs2);
       if (t + 1 >= kt_end) break;
-      step(t + 1, ks2, vs1, ks1, vs0);
+      step(gen, t + 1, ks2, vs1, ks1, vs0);
       if (t + 2 >= kt_end) break;
-      step(t + 2, ks0, vs2, ks2, vs1);
+      step(gen, t + 2, ks0, vs2, ks2, vs1);
       if (t + 3 >= kt_end) break;
-      step(t + 3, ks1, vs0, ks0, vs2);
+      step(gen, t + 3, ks1, vs0, ks0, vs2);
       if (t + 4 >= kt_end) break;
-      step(t + 4, ks2, vs1, ks1, vs0);
+      step(gen, t + 4, ks2, vs1, ks1, vs0);
       if (t + 5 >= kt_end) break;
-      step(t + 5, ks0, vs2, ks2, vs1);
+      step(gen, t + 5, ks0, vs2, ks2, vs1);
       if (t + 6 >= kt_end) break;
     }
   }
