@@ -239,9 +239,13 @@ def main():
                      "event_median_per_step": round(float(np.median(step_ms)), 4),
                      "event_min_per_step": round(min(step_ms), 4)},
     }
-    if t_fwd_step and t_merge and args.only in ("fwd", "all"):
+    if t_fwd_step and args.only in ("fwd", "all"):
+        # steps 1..7 fold their partial into the running result inside the step's own
+        # launch (ring_attn_fwd_step_merge); "merge" is only the final conversion, if any
         fwd_ms = per_step_ms["fwd_step"] + per_step_ms.get("merge", 0.0)
         extra["fwd_tflops"] = round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2)
+        # the merge entry point on its own, at the share's shape (the unfused path)
+        t_merge = time_lse_merge(torch, ra, dev, C, cfg.Hq, cfg.d)
         extra["merge"] = {"bytes_per_call": merge_bytes, "avg_us": round(t_merge * 1e3, 2),
                           "GB_per_s": round(merge_bytes / (t_merge * 1e-3) / 1e9, 1),
                           "frac_of_hbm_peak": round(merge_bytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -312,6 +316,27 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def time_lse_merge(torch, ra, dev, C, Hq, d, reps=20):
+    """Mean time (ms) of one lse_merge call (running and step results of the share's
+    shape, both live) on the current stream, from events around `reps` calls."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    o_acc = torch.randn((1, C, Hq, d), generator=g, device=dev)
+    o_step = torch.randn((1, C, Hq, d), generator=g, device=dev)
+    lse_acc = torch.randn((1, Hq, C), generator=g, device=dev) + 5.0
+    lse_step = torch.randn((1, Hq, C), generator=g, device=dev) + 5.0
+    ra.lse_merge(o_acc, lse_acc, o_step, lse_step)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        ra.lse_merge(o_acc, lse_acc, o_step, lse_step)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
 
 
 def packed_live_pairs(lengths, C, rank):

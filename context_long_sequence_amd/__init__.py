@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     ring_attn_bwd_preprocess,
     ring_attn_bwd_step,
     ring_attn_fwd_step,
+    ring_attn_fwd_step_merge,
     ring_recv_copy,
     segment_mask_from_pos,
 )

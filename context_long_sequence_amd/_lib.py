@@ -22,6 +22,7 @@ RA_DTYPE_BF16 = 1
 
 EXPORTED = (
     "ring_attn_fwd_step",
+    "ring_attn_fwd_step_merge",
     "lse_merge",
     "segment_mask_from_pos",
     "ring_attn_bwd_preprocess",
@@ -75,12 +76,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sp = ctypes.POINTER(RaShape)
     lib.ring_attn_fwd_step.argtypes = [sp, vp, vp, vp, vp, i64, vp, vp, vp]
+    lib.ring_attn_fwd_step_merge.argtypes = [sp, vp, vp, vp, vp, i64, vp, vp, vp, i32, vp]
     lib.lse_merge.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]
     lib.segment_mask_from_pos.argtypes = [i32, i64, vp, vp, vp]
     lib.ring_attn_bwd_preprocess.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.ring_attn_bwd_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
     lib.ring_recv_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
-    for fn in ("ring_attn_fwd_step", "lse_merge", "segment_mask_from_pos", "ring_attn_bwd_preprocess",
+    for fn in ("ring_attn_fwd_step", "ring_attn_fwd_step_merge", "lse_merge", "segment_mask_from_pos", "ring_attn_bwd_preprocess",
                "ring_attn_bwd_step", "ring_recv_copy"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.ra_status_string.argtypes = [ctypes.c_int]
@@ -165,6 +167,35 @@ def ring_attn_fwd_step(q, k, v, o_step, lse_step, *, q_offset: int, kv_offset: i
     _check("ring_attn_fwd_step", lib.ring_attn_fwd_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                                         _ptr(seg_ids), seg_len, _ptr(o_step),
                                                         _ptr(lse_step), _stream(stream)))
+
+
+def ring_attn_fwd_step_merge(q, k, v, o_acc, lse_acc, *, q_offset: int, kv_offset: int, causal: bool,
+                             scale: float, seg_ids: Optional[torch.Tensor] = None, o_out=None,
+                             stream=None) -> None:
+    """One ring step folded into the running result: (o_acc [B,Sq,Hq,d] fp32, lse_acc
+    [B,Hq,Sq] fp32) <- merge with the step's partial attention of q against k, v;
+    optionally the merged O converted to o_out's dtype (see include/ringattn.h)."""
+    B, Sq, Hq, d = q.shape
+    _need(q, "q", q.shape)
+    _need(k, "k", k.shape, q.dtype)
+    _need(v, "v", k.shape, q.dtype)
+    _need(o_acc, "o_acc", (B, Sq, Hq, d), torch.float32)
+    _need(lse_acc, "lse_acc", (B, Hq, Sq), torch.float32)
+    out_dtype = RA_DTYPE_F32
+    if o_out is not None:
+        _need(o_out, "o_out", (B, Sq, Hq, d))
+        out_dtype = _dtype_code(o_out)
+    seg_len = 0
+    if seg_ids is not None:
+        _need(seg_ids, "seg_ids", seg_ids.shape, torch.int32)
+        if seg_ids.dim() != 2 or seg_ids.shape[0] != B:
+            raise ValueError("seg_ids must be [B, seg_len]")
+        seg_len = seg_ids.shape[1]
+    shape = make_shape(q, k, q_offset, kv_offset, causal, scale)
+    lib = load()
+    _check("ring_attn_fwd_step_merge",
+           lib.ring_attn_fwd_step_merge(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(seg_ids), seg_len,
+                                        _ptr(o_acc), _ptr(lse_acc), _ptr(o_out), out_dtype, _stream(stream)))
 
 
 def lse_merge(o_acc, lse_acc, o_step=None, lse_step=None, o_out=None, stream=None) -> None:

@@ -53,7 +53,63 @@ struct FwdArgs {
   int causal;
   float scale_log2;  // softmax_scale * log2(e)
   int n_qtiles;
+  // Fused merge (ring_attn_fwd_step_merge): o and lse hold the running result and
+  // receive the merged one; o_out (optional) the merged O converted to out_kind
+  // (1 = fp32, 2 = bf16).
+  int merge;
+  void* o_out;
+  int out_kind;
 };
+
+// Epilogue of one query row held by this lane (both half-waves of the row call it):
+// the step's O = acc * inv in the vectors at columns 32*db + 8*r4 + 4*half, and its
+// LSE ls.  Stored as is, or merged into the running (o, lse) with the merge rule of
+// lse_merge (same functions, same bits) and optionally converted into o_out.  All
+// loads of the running row precede the stores (the pointers are restrict).
+template <int DB>
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, const f32x16 (&oacc)[DB], float inv, float ls,
+                                             int b, int hq, int qi, int half) {
+  constexpr int D = 32 * DB;
+  const int64_t row = ((int64_t)b * a.Sq + qi) * ((int64_t)a.Hq * D) + (int64_t)hq * D;
+  const int64_t li = ((int64_t)b * a.Hq + hq) * a.Sq + qi;
+  float* __restrict__ orow = a.o + row;
+  f32x4 os[DB][4];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      os[db][r4] = f32x4{oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv, oacc[db][4 * r4 + 2] * inv,
+                         oacc[db][4 * r4 + 3] * inv};
+  if (!a.merge) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * half) = os[db][r4];
+    if (half == 0) a.lse[li] = ls;
+    return;
+  }
+  const MergeWeights mw = merge_weights(a.lse[li], ls);
+  f32x4 o[DB][4];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) o[db][r4] = *reinterpret_cast<const f32x4*>(orow + 32 * db + 8 * r4 + 4 * half);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int c = 32 * db + 8 * r4 + 4 * half;
+      if (mw.live) {
+        o[db][r4] = merge_o(o[db][r4], os[db][r4], mw);
+        *reinterpret_cast<f32x4*>(orow + c) = o[db][r4];
+      }
+      if (a.out_kind == 1)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.o_out) + row + c) = o[db][r4];
+      else if (a.out_kind == 2)
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.o_out) + row + c) = to_bf16x4(o[db][r4]);
+    }
+  if (half == 0 && mw.live) a.lse[li] = mw.lse;
+}
 
 template <typename T, int D, bool kSeg>
 __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a) {
@@ -343,20 +399,7 @@ __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const bool live = l_tot > 0.0f;
   const float inv = live ? 1.0f / l_tot : 0.0f;
-  if (q_valid) {
-    float* orow = a.o + ((int64_t)b * a.Sq + qi) * q_row_stride + (int64_t)hq * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 v = {oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv, oacc[db][4 * r4 + 2] * inv,
-                   oacc[db][4 * r4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * half) = v;
-      }
-    }
-    if (half == 0)
-      a.lse[((int64_t)b * a.Hq + hq) * a.Sq + qi] = live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  }
+  if (q_valid) fwd_epilogue<DB>(a, oacc, inv, live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY, b, hq, qi, half);
 }
 
 
@@ -673,19 +716,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
   const float l_tot = half_sum(l_run);
   const bool live = l_tot > 0.0f;
   const float inv = live ? 1.0f / l_tot : 0.0f;
-  if (qv) {
-    float* orow = a.o + ((int64_t)b * a.Sq + qi) * q_rs + (int64_t)hq * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 v = {oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv, oacc[db][4 * r4 + 2] * inv,
-                   oacc[db][4 * r4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * half) = v;
-      }
-    if (half == 0)
-      a.lse[((int64_t)b * a.Hq + hq) * a.Sq + qi] = live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  }
+  if (qv) fwd_epilogue<4>(a, oacc, inv, live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY, b, hq, qi, half);
 }
 
 template <typename T, int D>
@@ -718,24 +749,20 @@ ra_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
 }  // namespace
 }  // namespace ra
 
-extern "C" ra_status ring_attn_fwd_step(const ra_shape* s, const void* q, const void* k, const void* v,
-                                        const int32_t* seg_ids, int64_t seg_len, float* o_step,
-                                        float* lse_step, void* stream) {
-  using namespace ra;
-  ra_status st = validate_step(s, seg_ids, seg_len);
-  if (st != RA_OK) return st;
-  if (!q || !k || !v || !o_step || !lse_step)
-    return fail(RA_ERR_INVALID_ARGUMENT, "q, k, v, o_step and lse_step must be non-NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_step) || !aligned16(lse_step))
-    return fail(RA_ERR_INVALID_ARGUMENT, "q, k, v, o_step and lse_step must be 16-byte aligned");
+namespace ra {
+namespace {
+
+ra_status fwd_entry(const ra_shape* s, const void* q, const void* k, const void* v, const int32_t* seg_ids,
+                    int64_t seg_len, float* o, float* lse, int merge, void* o_out, int out_kind,
+                    hipStream_t hs) {
   FwdArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
   a.seg = seg_ids;
   a.seg_len = seg_len;
-  a.o = o_step;
-  a.lse = lse_step;
+  a.o = o;
+  a.lse = lse;
   a.B = s->batch;
   a.Sq = s->q_len;
   a.Sk = s->kv_len;
@@ -746,11 +773,47 @@ extern "C" ra_status ring_attn_fwd_step(const ra_shape* s, const void* q, const 
   a.causal = s->causal;
   a.scale_log2 = s->softmax_scale * kLog2e;
   a.n_qtiles = (s->q_len + kBM - 1) / kBM;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+  a.merge = merge;
+  a.o_out = o_out;
+  a.out_kind = out_kind;
   if (s->dtype == RA_DTYPE_BF16) {
     if (s->head_dim == 128) return launch_fwd<__bf16, 128>(a, hs);
     return launch_fwd<__bf16, 64>(a, hs);
   }
   if (s->head_dim == 128) return launch_fwd<float, 128>(a, hs);
   return launch_fwd<float, 64>(a, hs);
+}
+
+}  // namespace
+}  // namespace ra
+
+extern "C" ra_status ring_attn_fwd_step(const ra_shape* s, const void* q, const void* k, const void* v,
+                                        const int32_t* seg_ids, int64_t seg_len, float* o_step,
+                                        float* lse_step, void* stream) {
+  using namespace ra;
+  ra_status st = validate_step(s, seg_ids, seg_len);
+  if (st != RA_OK) return st;
+  if (!q || !k || !v || !o_step || !lse_step)
+    return fail(RA_ERR_INVALID_ARGUMENT, "q, k, v, o_step and lse_step must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_step) || !aligned16(lse_step))
+    return fail(RA_ERR_INVALID_ARGUMENT, "q, k, v, o_step and lse_step must be 16-byte aligned");
+  return fwd_entry(s, q, k, v, seg_ids, seg_len, o_step, lse_step, 0, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+extern "C" ra_status ring_attn_fwd_step_merge(const ra_shape* s, const void* q, const void* k, const void* v,
+                                              const int32_t* seg_ids, int64_t seg_len, float* o_acc,
+                                              float* lse_acc, void* o_out, int32_t out_dtype, void* stream) {
+  using namespace ra;
+  ra_status st = validate_step(s, seg_ids, seg_len);
+  if (st != RA_OK) return st;
+  if (!q || !k || !v || !o_acc || !lse_acc)
+    return fail(RA_ERR_INVALID_ARGUMENT, "q, k, v, o_acc and lse_acc must be non-NULL");
+  if (o_out && out_dtype != RA_DTYPE_F32 && out_dtype != RA_DTYPE_BF16)
+    return fail(RA_ERR_UNSUPPORTED, "out_dtype %d is not supported", out_dtype);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_acc) || !aligned16(lse_acc) ||
+      (o_out && ((uintptr_t)o_out & 7u)))
+    return fail(RA_ERR_INVALID_ARGUMENT, "misaligned pointer (16 bytes; o_out 8 bytes)");
+  const int out_kind = o_out == nullptr ? 0 : (out_dtype == RA_DTYPE_F32 ? 1 : 2);
+  return fwd_entry(s, q, k, v, seg_ids, seg_len, o_acc, lse_acc, 1, o_out, out_kind,
+                   static_cast<hipStream_t>(stream));
 }

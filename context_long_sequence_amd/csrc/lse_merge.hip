@@ -33,29 +33,17 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int Sq, int Hq, int
     f32x4 o = acc4[t];
     if constexpr (kMerge) {
       const int64_t li = ((int64_t)b * Hq + h) * Sq + i;
-      const float L = lse_acc[li];
-      const float Ls = lse_step[li];
-      const float m = fmaxf(L, Ls);
-      if (m != -INFINITY) {
-        const float w = __expf(L - m);    // 0 when L = -inf
-        const float ws = __expf(Ls - m);  // 0 when Ls = -inf
-        const float tot = w + ws;
-        const float inv = 1.0f / tot;
-        const f32x4 os = reinterpret_cast<const f32x4*>(o_step)[base4 + t];
-        const f32x4 term_s = os * (ws * inv);
-        o = (w == 0.0f) ? term_s : (ws == 0.0f ? o : o * (w * inv) + term_s);
+      const MergeWeights mw = merge_weights(lse_acc[li], lse_step[li]);
+      if (mw.live) {
+        o = merge_o(o, reinterpret_cast<const f32x4*>(o_step)[base4 + t], mw);
         acc4[t] = o;
-        if (t - h * d4 == 0) lse_acc[li] = m + __logf(tot);
+        if (t - h * d4 == 0) lse_acc[li] = mw.lse;
       }
     }
     if constexpr (kOut == 1) {
       reinterpret_cast<f32x4*>(o_out)[base4 + t] = o;
     } else if constexpr (kOut == 2) {
-      f32x2 p0 = {o[0], o[1]}, p1 = {o[2], o[3]};
-      bf16x2 r0 = __builtin_convertvector(p0, bf16x2);
-      bf16x2 r1 = __builtin_convertvector(p1, bf16x2);
-      bf16x4 r = {r0[0], r0[1], r1[0], r1[1]};
-      reinterpret_cast<bf16x4*>(o_out)[base4 + t] = r;
+      reinterpret_cast<bf16x4*>(o_out)[base4 + t] = to_bf16x4(o);
     }
   }
 }

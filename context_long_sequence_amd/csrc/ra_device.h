@@ -174,6 +174,43 @@ __device__ __forceinline__ void buffer_load_lds16(buffer_rsrc rs, void* dst, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, voffset, 0, 0, 0);
 }
 
+// Merge of two partial results of the same query row over disjoint key sets: the
+// running (L, O) and a step's (Ls, Os), log-sum-exps in natural log.  With
+// M = max(L, Ls): L' = M + ln(e^(L-M) + e^(Ls-M)), O' = e^(L-L') O + e^(Ls-L') Os.
+// Both -inf (no key seen yet): `live` is false and the pair stays as it is.  The
+// merge kernel and the forward step's fused epilogue share these two functions, so
+// both give the same bits.
+struct MergeWeights {
+  float w, ws, inv, lse;
+  bool live;
+};
+__device__ __forceinline__ MergeWeights merge_weights(float L, float Ls) {
+  MergeWeights r;
+  const float m = fmaxf(L, Ls);
+  r.live = m != -INFINITY;
+  if (!r.live) {
+    r.w = r.ws = r.inv = 0.0f;
+    r.lse = -INFINITY;
+    return r;
+  }
+  r.w = __expf(L - m);    // 0 when L = -inf
+  r.ws = __expf(Ls - m);  // 0 when Ls = -inf
+  const float tot = r.w + r.ws;
+  r.inv = 1.0f / tot;
+  r.lse = m + __logf(tot);
+  return r;
+}
+__device__ __forceinline__ f32x4 merge_o(f32x4 o, f32x4 os, const MergeWeights& mw) {
+  const f32x4 term_s = os * (mw.ws * mw.inv);
+  return (mw.w == 0.0f) ? term_s : (mw.ws == 0.0f ? o : o * (mw.w * mw.inv) + term_s);
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 o) {
+  const f32x2 p0 = {o[0], o[1]}, p1 = {o[2], o[3]};
+  const bf16x2 r0 = __builtin_convertvector(p0, bf16x2);
+  const bf16x2 r1 = __builtin_convertvector(p1, bf16x2);
+  return bf16x4{r0[0], r0[1], r1[0], r1[1]};
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8).  waitcnt_vm(n): at most n vector-memory operations outstanding;
 // waitcnt_vm_lgkm0(n): the same and no LDS operation outstanding.

@@ -79,4 +79,4 @@ extern "C" const char* ra_status_string(ra_status st) {
 
 extern "C" const char* ra_last_error(void) { return ra::g_last_error; }
 
-extern "C" int32_t ra_abi_version(void) { return 2; }
+extern "C" int32_t ra_abi_version(void) { return 3; }

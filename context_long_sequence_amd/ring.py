@@ -29,18 +29,40 @@ def _scale(d: int, scale: Optional[float]) -> float:
 
 
 class RingWorkspace:
-    """Device temporaries of the ring loops (the only memory beyond inputs/outputs).
+    """Device temporaries of the ring loops (the only memory beyond inputs/outputs):
+    the fp32 running O of the forward (each step's partial is folded into it inside
+    the step's launch, so no per-step buffer exists) and the backward's delta.
     Sized O(Sq * Hq * d); reusable across calls of the same shape."""
 
     def __init__(self, B: int, Sq: int, Hq: int, d: int, device, backward: bool = False):
-        self.o_step = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=device)
-        self.lse_step = torch.empty((B, Hq, Sq), dtype=torch.float32, device=device)
         self.o_acc = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=device)
         self.delta = torch.empty((B, Hq, Sq), dtype=torch.float32, device=device) if backward else None
 
     def nbytes(self) -> int:
-        ts = [self.o_step, self.lse_step, self.o_acc, self.delta]
+        ts = [self.o_acc, self.delta]
         return sum(t.numel() * t.element_size() for t in ts if t is not None)
+
+
+def _fold_step(q, kc, vc, o_acc, lse_acc, first: bool, last: bool, out, *, q_offset: int, kv_offset: int,
+               causal: bool, scale: float, seg_ids, stream, step_hook=None, step: int = 0):
+    """One ring step into the running (o_acc, lse_acc): the first step writes it
+    (ring_attn_fwd_step), every later one folds its partial into it in the same
+    launch (ring_attn_fwd_step_merge); the last step also writes `out` (q's dtype)."""
+    if first:
+        _lib.ring_attn_fwd_step(q, kc, vc, o_acc, lse_acc, q_offset=q_offset, kv_offset=kv_offset, causal=causal,
+                                scale=scale, seg_ids=seg_ids, stream=stream)
+        if step_hook is not None:
+            step_hook("fwd_step", step)
+        if last:  # a single step: only the conversion
+            _lib.lse_merge(o_acc, lse_acc, None, None, o_out=out, stream=stream)
+            if step_hook is not None:
+                step_hook("merge", step)
+    else:
+        _lib.ring_attn_fwd_step_merge(q, kc, vc, o_acc, lse_acc, q_offset=q_offset, kv_offset=kv_offset,
+                                      causal=causal, scale=scale, seg_ids=seg_ids, o_out=out if last else None,
+                                      stream=stream)
+        if step_hook is not None:
+            step_hook("fwd_step", step)
 
 
 def ring_forward(q_local: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chunks: Sequence[torch.Tensor],
@@ -62,23 +84,12 @@ def ring_forward(q_local: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chun
         out = torch.empty_like(q_local)
     if lse is None:
         lse = torch.empty((B, Hq, C), dtype=torch.float32, device=q_local.device)
-    o_acc = ws.o_acc
     q_offset = rank * C
     for i, c in enumerate(ring_schedule(rank, cp)):
         kc, vc = k_chunks[c], v_chunks[c]
-        first = i == 0
-        _lib.ring_attn_fwd_step(q_local, kc, vc, o_acc if first else ws.o_step, lse if first else ws.lse_step,
-                                q_offset=q_offset, kv_offset=c * kc.shape[1], causal=causal, scale=sc,
-                                seg_ids=seg_ids, stream=stream)
-        if step_hook is not None:
-            step_hook("fwd_step", i)
-        last = i == cp - 1
-        if not first:
-            _lib.lse_merge(o_acc, lse, ws.o_step, ws.lse_step, o_out=out if last else None, stream=stream)
-            if step_hook is not None:
-                step_hook("merge", i)
-        elif last:
-            _lib.lse_merge(o_acc, lse, None, None, o_out=out, stream=stream)
+        _fold_step(q_local, kc, vc, ws.o_acc, lse, i == 0, i == cp - 1, out, q_offset=q_offset,
+                   kv_offset=c * kc.shape[1], causal=causal, scale=sc, seg_ids=seg_ids, stream=stream,
+                   step_hook=step_hook, step=i)
     return out, lse
 
 
@@ -151,17 +162,15 @@ def zigzag_pairs(rank: int, cp: int, h: int, causal: bool = True) -> List[Tuple[
 
 
 class ZigzagWorkspace:
-    """Device temporaries of the balanced-layout ring loops: per-half accumulators,
-    one step buffer, the backward's delta ([2, Hq, h]: one row block per half)."""
+    """Device temporaries of the balanced-layout ring loops: per-half running O and
+    the backward's delta ([2, Hq, h]: one row block per half)."""
 
     def __init__(self, h: int, Hq: int, d: int, device, backward: bool = False):
-        self.o_step = torch.empty((1, h, Hq, d), dtype=torch.float32, device=device)
-        self.lse_step = torch.empty((1, Hq, h), dtype=torch.float32, device=device)
         self.o_acc = torch.empty((2, h, Hq, d), dtype=torch.float32, device=device)
         self.delta = torch.empty((2, Hq, h), dtype=torch.float32, device=device) if backward else None
 
     def nbytes(self) -> int:
-        ts = [self.o_step, self.lse_step, self.o_acc, self.delta]
+        ts = [self.o_acc, self.delta]
         return sum(t.numel() * t.element_size() for t in ts if t is not None)
 
 
@@ -200,20 +209,9 @@ def ring_forward_zigzag(q_local: torch.Tensor, k_ranks: Sequence[torch.Tensor], 
     for n, (i, c, j, k) in enumerate(pairs):
         kh = zigzag_halves(c, cp)
         acc, lacc = ws.o_acc[j:j + 1], lse[j:j + 1]
-        first = not seen[j]
-        _lib.ring_attn_fwd_step(_half(q_local, j, h), _half(k_ranks[c], k, h), _half(v_ranks[c], k, h),
-                                acc if first else ws.o_step, lacc if first else ws.lse_step,
-                                q_offset=qh[j] * h, kv_offset=kh[k] * h, causal=causal, scale=sc,
-                                seg_ids=seg_ids, stream=stream)
-        if step_hook is not None:
-            step_hook("fwd_step", i)
-        last = last_of[j] == n
-        if not first:
-            _lib.lse_merge(acc, lacc, ws.o_step, ws.lse_step, o_out=_half(out, j, h) if last else None, stream=stream)
-            if step_hook is not None:
-                step_hook("merge", i)
-        elif last:
-            _lib.lse_merge(acc, lacc, None, None, o_out=_half(out, j, h), stream=stream)
+        _fold_step(_half(q_local, j, h), _half(k_ranks[c], k, h), _half(v_ranks[c], k, h), acc, lacc,
+                   not seen[j], last_of[j] == n, _half(out, j, h), q_offset=qh[j] * h, kv_offset=kh[k] * h,
+                   causal=causal, scale=sc, seg_ids=seg_ids, stream=stream, step_hook=step_hook, step=i)
         seen[j] = True
     for j in range(2):
         if not seen[j]:  # no visible key at all (not reachable under the causal rule)
@@ -338,17 +336,11 @@ def ring_forward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Tens
         else:
             compute.wait_event(received[i % 2])
             kc, vc = sl.k[i % 2], sl.v[i % 2]
-        first, last = i == 0, i == cp - 1
-        _lib.ring_attn_fwd_step(q_local, kc, vc, o_acc if first else ws.o_step, lse if first else ws.lse_step,
-                                q_offset=rank * C, kv_offset=c * kc.shape[1], causal=causal, scale=sc,
-                                seg_ids=seg_ids, stream=compute)
+        _fold_step(q_local, kc, vc, o_acc, lse, i == 0, i == cp - 1, out, q_offset=rank * C,
+                   kv_offset=c * kc.shape[1], causal=causal, scale=sc, seg_ids=seg_ids, stream=compute)
         if i > 0:
             released[i % 2] = torch.cuda.Event()
             released[i % 2].record(compute)
-        if not first:
-            _lib.lse_merge(o_acc, lse, ws.o_step, ws.lse_step, o_out=out if last else None, stream=compute)
-        elif last:
-            _lib.lse_merge(o_acc, lse, None, None, o_out=out, stream=compute)
     return out, lse
 
 

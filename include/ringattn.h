@@ -117,6 +117,29 @@ ra_status lse_merge(int32_t batch, int32_t q_len, int32_t heads_q, int32_t head_
                     int32_t out_dtype, void* stream);
 
 /*
+ * ring_attn_fwd_step_merge — ring_attn_fwd_step and lse_merge of its result in one
+ * launch (axolotl docs "Sequence Parallelism": the per-chunk results are
+ * aggregated as they travel around the ring).  The step's partial (O_s, LSE_s) of
+ * the local queries against this KV chunk, defined as for ring_attn_fwd_step, is
+ * folded into the running (o_acc, lse_acc) in place with the lse_merge rule and is
+ * never written out.  Equal, bit for bit, to ring_attn_fwd_step into scratch
+ * followed by lse_merge(o_acc, lse_acc, scratch, ..., o_out, out_dtype).
+ *  shape, q, k, v, seg_ids, seg_len: as ring_attn_fwd_step.
+ *  o_acc    [B, Sq, Hq, d] fp32, read and written;  lse_acc [B, Hq, Sq] fp32, read
+ *           and written (natural log; -inf for rows that have seen no key yet).
+ *  o_out    NULL, or [B, Sq, Hq, d] in out_dtype (RA_DTYPE_F32 or RA_DTYPE_BF16,
+ *           round to nearest even): the merged O (the last ring step's output).
+ * o_acc/lse_acc must not overlap q, k, v or o_out; one call per running result at
+ * a time (the call reads and writes it).
+ * Errors: as ring_attn_fwd_step (with o_acc/lse_acc in place of o_step/lse_step);
+ * RA_ERR_UNSUPPORTED for an unknown out_dtype; RA_ERR_INVALID_ARGUMENT for o_out
+ * not 8-byte aligned.
+ */
+ra_status ring_attn_fwd_step_merge(const ra_shape* shape, const void* q, const void* k, const void* v,
+                                   const int32_t* seg_ids, int64_t seg_len, float* o_acc, float* lse_acc,
+                                   void* o_out, int32_t out_dtype, void* stream);
+
+/*
  * segment_mask_from_pos — sample (segment) id of every token of packed rows:
  *   seg_ids[b, t] = #{t' <= t : position_ids[b, t'] == 0} - 1,
  * computed over the GLOBAL row so that a context-parallel chunk that starts in
@@ -180,7 +203,7 @@ const char* ra_status_string(ra_status status);
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* ra_last_error(void);
 
-/* Library ABI version: 2 (2 added ring_recv_copy). */
+/* Library ABI version: 3 (2 added ring_recv_copy, 3 ring_attn_fwd_step_merge). */
 int32_t ra_abi_version(void);
 
 #ifdef __cplusplus

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.ra_abi_version() == 2
+    assert lib.ra_abi_version() == 3
     assert lib.ra_status_string(0) == b"RA_OK"
     assert lib.ra_status_string(2) == b"RA_ERR_UNSUPPORTED"
 
@@ -99,6 +99,26 @@ def test_merge_segment_preprocess_validation(lib):
     assert lib.segment_mask_from_pos(1, 1 << 40, FAKE, FAKE, None) == 1
     assert lib.ring_attn_bwd_preprocess(1, 4, 4, 96, 1, FAKE, FAKE, FAKE, None) == 2
     assert lib.ring_attn_bwd_preprocess(1, 4, 4, 128, 5, FAKE, FAKE, FAKE, None) == 2
+
+
+@pytest.mark.parametrize("kw,status", [(dict(head_dim=96), 2), (dict(heads_q=3), 1), (dict(q_len=0), 1)])
+def test_fwd_step_merge_rejects_invalid_shapes(lib, kw, status):
+    s = _shape(**kw)
+    assert lib.ring_attn_fwd_step_merge(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, None, 0, None) == status
+
+
+def test_fwd_step_merge_validation(lib):
+    s = _shape()
+    # NULL running result
+    assert lib.ring_attn_fwd_step_merge(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, None, FAKE, None, 0, None) == 1
+    assert lib.ring_attn_fwd_step_merge(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, FAKE, None, None, 0, None) == 1
+    # unknown output dtype; o_out not 8-byte aligned; misaligned running result
+    assert lib.ring_attn_fwd_step_merge(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, FAKE, 9, None) == 2
+    assert lib.ring_attn_fwd_step_merge(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, FAKE + 4, 1,
+                                        None) == 1
+    assert lib.ring_attn_fwd_step_merge(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, FAKE + 8, FAKE, None, 0,
+                                        None) == 1
+    assert b"misaligned" in lib.ra_last_error()
 
 
 def test_recv_copy_rejects_null_pointers(lib):

@@ -226,6 +226,42 @@ def test_bwd_step(case):
     report("bwd_step", case=case, **errs)
 
 
+@pytest.mark.parametrize("out", [None, "same", "f32"])
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_fwd_step_merge_equals_step_then_merge(case, out):
+    """ring_attn_fwd_step_merge gives the same bits as ring_attn_fwd_step followed by
+    lse_merge: running result with live rows, rows that have seen no key yet
+    (LSE = -inf), and steps whose rows see no key of the chunk."""
+    ra = lib()
+    dtype, B, Sq, Sk, Hq, Hkv, d, q_off, kv_off, causal, packed = case
+    q, k, v, seg, S = _step_case(case, 31 + Sq + Sk)
+    rng = np.random.default_rng(7 + Sk)
+    o0 = rng.standard_normal((B, Sq, Hq, d)).astype(np.float32)
+    l0 = (rng.standard_normal((B, Hq, Sq)) + 3.0).astype(np.float32)
+    l0[:, :, ::5] = -np.inf
+    qd, kd, vd = to_dev(q, TD[dtype]), to_dev(k, TD[dtype]), to_dev(v, TD[dtype])
+    segd = None if seg is None else to_dev(seg, torch.int32)
+    kw = dict(q_offset=q_off, kv_offset=kv_off, causal=causal, scale=1 / math.sqrt(d), seg_ids=segd)
+    out_dtype = None if out is None else (TD[dtype] if out == "same" else torch.float32)
+
+    def new_out():
+        return None if out_dtype is None else torch.full((B, Sq, Hq, d), float("nan"), dtype=out_dtype,
+                                                         device=device())
+
+    oa, la, outa = to_dev(o0, torch.float32), to_dev(l0, torch.float32), new_out()
+    o_s = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=device())
+    l_s = torch.empty((B, Hq, Sq), dtype=torch.float32, device=device())
+    ra.ring_attn_fwd_step(qd, kd, vd, o_s, l_s, **kw)
+    ra.lse_merge(oa, la, o_s, l_s, o_out=outa)
+    ob, lb, outb = to_dev(o0, torch.float32), to_dev(l0, torch.float32), new_out()
+    ra.ring_attn_fwd_step_merge(qd, kd, vd, ob, lb, o_out=outb, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
+    assert torch.equal(la, lb)
+    if outa is not None:
+        assert torch.equal(outa, outb)
+
+
 WIDE_CASES = [
     # (Sq, Sk, q_off, kv_off, causal): 128 query heads x ceil(Sq / 256) >= 1024 query tiles
     # of 256 rows, the grid size at which the bf16 d=128 forward uses 8-wave workgroups.
