@@ -97,6 +97,11 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
   const float lse_q = q_valid ? a.lse[li] : -INFINITY;
   const float neg_lse2 = lse_q == -INFINITY ? -INFINITY : -lse_q * kLog2e;
   const float dl = q_valid ? a.delta[li] : 0.0f;
+  // The dP^T chain starts from -delta (every register of the lane holds its query's
+  // -delta), so it yields dP - delta with no subtraction per element.
+  f32x16 neg_dl16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) neg_dl16[i] = -dl;
 
   // Visibility of key k0 + 16*half + i: i <= lim_base - k0 (causal rule, clamped to
   // +-2^30 so that 32-bit arithmetic is exact; rows past Sq see nothing) and
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
       const char* vb = reinterpret_cast<const char*>(vt_);
 
       // S^T = K Q^T and dP^T = V dO^T; register i of half h = key k0 + 16h + i.
-      f32x16 st = f32x16{}, dpt = f32x16{};
+      f32x16 st = f32x16{}, dpt = neg_dl16;
       {
         bf16x8 fk[8], fv[8];
 #pragma unroll
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dpt[i] - dl);
+      for (int i = 0; i < 16; ++i) ds[i] = p[i] * dpt[i];
       // dQ^T += K^T dS^T: K^T rows (keys 16h + 8m + j) by transposing reads of the K tile.
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
