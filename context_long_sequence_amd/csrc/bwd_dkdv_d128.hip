@@ -55,7 +55,10 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   const int64_t q_rs = (int64_t)a.Hq * kD, kv_rs = (int64_t)a.Hkv * kD;
   const int q_rb = a.Hq * kD * 2;  // bytes between consecutive query rows
 
-  // K and V of this lane's key as B operands of S = Q K^T and dP = dO V^T.
+  // K and V of this lane's key as B operands of S = Q K^T and dP = dO V^T.  V is
+  // negated (sign bits flipped, exact): the dP chain starts from delta and yields
+  // delta - dP, so dS comes out negated with no subtraction per element (undone
+  // in the final dK store).
   bf16x8 kf[8], vf[8];
   {
     const int64_t off = ((int64_t)b * a.Sk + (k_valid ? kj : 0)) * kv_rs + (int64_t)g * kD + 8 * half;
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       kf[s] = k_valid ? load_bf16x8(kp + 16 * s) : bf16x8{};
-      vf[s] = k_valid ? load_bf16x8(vp + 16 * s) : bf16x8{};
+      vf[s] = k_valid ? neg_bf16x8(load_bf16x8(vp + 16 * s)) : bf16x8{};
     }
   }
 
@@ -251,7 +254,8 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     bf16x8 fq[2][8], fd[2][8];            // A operands of the score MFMAs
     bf16x8 dot[2][2][4], qtf[2][2][4];    // [qb][m][db]: dO^T and Q^T operands
     bf16x8 pf[2][2], sf[2][2];            // [qb][m]: packed P and dS, elements 8m..8m+7
-    float lq[2][16], dl[2][16];           // -LSE*log2(e) and delta of the block's queries
+    float lq[2][16];                      // -LSE*log2(e) of the block's queries
+    f32x16 dlv[2];                        // delta of the block's queries: the dP chain's start
     int sgq[2][16];                       // segment ids of the block's queries (packed rows)
     float ea[2][16], eb[2][16];           // element pipeline registers
     float pe[2][16], de[2][16];           // P and dS
@@ -264,7 +268,6 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         lq[qb][i] = xs[32 * qb + 16 * half + i];
-        dl[qb][i] = xs[QT + 32 * qb + 16 * half + i];
         if constexpr (kMask && kSeg) sgq[qb][i] = __builtin_bit_cast(int, xs[2 * QT + 32 * qb + 16 * half + i]);
       }
     };
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     };
     auto stage_b = [&](int qb, int i) {
       float x = __builtin_fmaf(ea[qb][i], a.scale_log2, lq[qb][i]);
-      float y = eb[qb][i] - dl[qb][i];
+      float y = eb[qb][i];
       if constexpr (kMask) {
         const int q0 = qtile0 + 32 * qb;
         bool vis = (i >= vis_lo - q0) & (i < vis_hi - q0);
@@ -326,16 +329,22 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     };
 
     // P1: block 0 scores; block 1 operand reads in their shadow.
+    auto read_delta = [&](int qb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dlv[qb][i] = xs[QT + 32 * qb + 16 * half + i];
+    };
+    read_delta(0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) read_op(0, c);
     fence();
     s[0] = f32x16{};
-    dp[0] = f32x16{};
+    dp[0] = dlv[0];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       s[0] = mfma_bf16(fq[0][c], kf[c], s[0]);
       fq[1][c] = load_bf16x8(qc + 8192 + (rA ^ (c << 5)));
       if (c == 2) read_rows(0);
+      if (c == 5) read_delta(1);
       fence();
       dp[0] = mfma_bf16(fd[0][c], vf[c], dp[0]);
       fd[1][c] = load_bf16x8(dc + 8192 + (rA ^ (c << 5)));
@@ -346,7 +355,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     // P2: block 1 scores; block 0 elements 0..15 (stages up to slot 15), its m = 0
     // transposed operands, and the packing of its elements 0..7.
     s[1] = f32x16{};
-    dp[1] = f32x16{};
+    dp[1] = dlv[1];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       if (k % 2 == 0)
@@ -450,7 +459,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   // loads of a group are in flight together (the two pointers do not alias).
   float* __restrict__ dkp = a.dk;
   float* __restrict__ dvp = a.dv;
-  const float ks = a.scale;
+  const float ks = -a.scale;  // dk holds -sum dS^T q (the dP chain runs on negated V)
   const int64_t base = ((int64_t)b * a.Sk + kw) * kv_rs + (int64_t)g * kD + col;
   const bool full = kw + 32 <= a.Sk;
 #pragma unroll

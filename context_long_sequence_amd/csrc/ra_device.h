@@ -41,6 +41,12 @@ __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Negation of 8 bf16 values (sign bits flipped: exact).
+__device__ __forceinline__ bf16x8 neg_bf16x8(bf16x8 v) {
+  const u32x4 m = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) ^ m);
+}
+
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
