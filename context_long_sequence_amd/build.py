@@ -40,9 +40,9 @@ def compile_flags():
     ]
 
 
-# Per-file compile flag adjustments.  The dK/dV kernel keeps its accumulators in
-# AGPRs (they are touched only by MFMAs inside its loop), which frees VGPRs.
-_DROP_FLAGS = {"bwd_dkdv_d128.hip": ("-mllvm", "-amdgpu-mfma-vgpr-form")}
+# Per-file compile flag adjustments (none at present: the dK/dV kernel keeps its
+# dK/dV accumulators in AGPRs through inline-asm MFMAs instead).
+_DROP_FLAGS = {}
 
 
 def flags_for(src: str):

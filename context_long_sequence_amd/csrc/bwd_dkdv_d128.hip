@@ -10,6 +10,7 @@
 // ALU pipeline (see compute below).
 #include "bwd_d128.h"
 
+
 namespace ra {
 namespace {
 
@@ -228,15 +229,17 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   // SIMD the vector ALU only runs beside the matrix unit if the instruction stream
   // interleaves them and the vector instructions between two MFMAs do not depend on
   // one another, so the tile is one straight-line body of 64 MFMA slots pinned with
-  // scheduling fences, and each element passes through four stages in four
-  // consecutive slots (A: copy S and dP out of the accumulation registers; B: the
-  // exponent S*scale*log2(e) - LSE*log2(e), dP - delta and, in the masked body, the
-  // mask; C: exp2; D: dS = P * (dP - delta)):
+  // scheduling fences, and each element passes through three stages in three
+  // consecutive slots (B: the exponent S*scale*log2(e) - LSE*log2(e) and, in the
+  // masked body, the mask; C: exp2; D: -dS = P * (delta - dP)):
   //   P1: block 0 scores                  | block 1 operand reads
   //   P2: block 1 scores                  | block 0 elements, dO^T/Q^T reads
-  //   P3: block 0 gradients               | block 1 elements (and block 0's last 3)
-  //   P4: block 1 gradients               | block 1's last 3 elements
-  // A slot then holds at most six independent vector instructions besides its MFMA.
+  //   P3: block 0 gradients               | block 1 elements (and block 0's last 2)
+  //   P4: block 1 gradients               | block 1's last 2 elements
+  // The score MFMAs write vector registers (read by the stages directly); the
+  // gradient MFMAs accumulate dK and dV in AGPRs through inline asm (mfma_acc), since
+  // the compiler gives all MFMAs of a function one register form.  A slot then holds
+  // at most six independent vector instructions besides its MFMA.
   // The masked body (kMask) sets the exponent of every invisible element to -inf, so
   // P and dS are exactly 0 there: the causal rule, the ends of the query shard and
   // of the chunk and, for packed rows, the segment test.  P uses the final LSE as
@@ -250,19 +253,23 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     const int qtile0 = qt_cur * QT;
     const char* qc = reinterpret_cast<const char*>(qt_);
     const char* dc = reinterpret_cast<const char*>(dt_);
-    f32x16 s[2], dp[2];
+    f32x16 s[2], dp[2];                   // S and delta - dP of the two blocks (vector registers)
     bf16x8 fq[2][8], fd[2][8];            // A operands of the score MFMAs
     bf16x8 dot[2][2][4], qtf[2][2][4];    // [qb][m][db]: dO^T and Q^T operands
-    bf16x8 pf[2][2], sf[2][2];            // [qb][m]: packed P and dS, elements 8m..8m+7
+    bf16x8 pf[2][2], sf[2][2];            // [qb][m]: packed P and -dS, elements 8m..8m+7
     float lq[2][16];                      // -LSE*log2(e) of the block's queries
     f32x16 dlv[2];                        // delta of the block's queries: the dP chain's start
     int sgq[2][16];                       // segment ids of the block's queries (packed rows)
-    float ea[2][16], eb[2][16];           // element pipeline registers
-    float pe[2][16], de[2][16];           // P and dS
+    float ea[2][16];                      // element pipeline register (exponent)
+    float pe[2][16], de[2][16];           // P and -dS
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
     auto read_op = [&](int qb, int c) {
       fq[qb][c] = load_bf16x8(qc + 8192 * qb + (rA ^ (c << 5)));
       fd[qb][c] = load_bf16x8(dc + 8192 * qb + (rA ^ (c << 5)));
+    };
+    auto read_delta = [&](int qb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dlv[qb][i] = xs[QT + 32 * qb + 16 * half + i];
     };
     auto read_rows = [&](int qb) {
 #pragma unroll
@@ -279,25 +286,17 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
       dot[qb][m][db] = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
       qtf[qb][m][db] = bf16x8{q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
     };
-    // Element stages; the empty statements keep each stage's results in its slot.
-    auto stage_a = [&](int qb, int i) {
-      float x = s[qb][i], y = dp[qb][i];
-      asm volatile("" : "+v"(x), "+v"(y));
-      ea[qb][i] = x;
-      eb[qb][i] = y;
-    };
+    // Element stages; the empty statements keep each stage's result in its slot.
     auto stage_b = [&](int qb, int i) {
-      float x = __builtin_fmaf(ea[qb][i], a.scale_log2, lq[qb][i]);
-      float y = eb[qb][i];
+      float x = __builtin_fmaf(s[qb][i], a.scale_log2, lq[qb][i]);
       if constexpr (kMask) {
         const int q0 = qtile0 + 32 * qb;
         bool vis = (i >= vis_lo - q0) & (i < vis_hi - q0);
         if constexpr (kSeg) vis &= sgq[qb][i] == seg_k;
         x = vis ? x : -__builtin_inff();
       }
-      asm volatile("" : "+v"(x), "+v"(y));
+      asm volatile("" : "+v"(x));
       ea[qb][i] = x;
-      eb[qb][i] = y;
     };
     auto stage_c = [&](int qb, int i) {
       float x = exp2_fast(ea[qb][i]);
@@ -305,18 +304,17 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
       pe[qb][i] = x;
     };
     auto stage_d = [&](int qb, int i) {
-      float y = pe[qb][i] * eb[qb][i];
+      float y = pe[qb][i] * dp[qb][i];
       asm volatile("" : "+v"(y));
       de[qb][i] = y;
     };
-    // The stages of block qb that fall in its k-th element slot (k = 0 .. 18).
+    // The stages of block qb that fall in its k-th element slot (k = 0 .. 17).
     auto elements = [&](int qb, int k) {
-      if (k >= 3 && k < 19) stage_d(qb, k - 3);
-      if (k >= 2 && k < 18) stage_c(qb, k - 2);
-      if (k >= 1 && k < 17) stage_b(qb, k - 1);
-      if (k < 16) stage_a(qb, k);
+      if (k >= 2 && k < 18) stage_d(qb, k - 2);
+      if (k >= 1 && k < 17) stage_c(qb, k - 1);
+      if (k < 16) stage_b(qb, k);
     };
-    // bf16 packing of elements 8m + 2j, 8m + 2j + 1 (j = 0 .. 3) of P and dS.
+    // bf16 packing of elements 8m + 2j, 8m + 2j + 1 (j = 0 .. 3) of P and -dS.
     auto pack = [&](int qb, int m, int j) {
       const f32x2 p2 = {pe[qb][8 * m + 2 * j], pe[qb][8 * m + 2 * j + 1]};
       const f32x2 d2 = {de[qb][8 * m + 2 * j], de[qb][8 * m + 2 * j + 1]};
@@ -329,42 +327,35 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     };
 
     // P1: block 0 scores; block 1 operand reads in their shadow.
-    auto read_delta = [&](int qb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dlv[qb][i] = xs[QT + 32 * qb + 16 * half + i];
-    };
     read_delta(0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) read_op(0, c);
     fence();
-    s[0] = f32x16{};
-    dp[0] = dlv[0];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      s[0] = mfma_bf16(fq[0][c], kf[c], s[0]);
+      s[0] = mfma_bf16(fq[0][c], kf[c], c == 0 ? f32x16{} : s[0]);
       fq[1][c] = load_bf16x8(qc + 8192 + (rA ^ (c << 5)));
       if (c == 2) read_rows(0);
       if (c == 5) read_delta(1);
       fence();
-      dp[0] = mfma_bf16(fd[0][c], vf[c], dp[0]);
+      dp[0] = mfma_bf16(fd[0][c], vf[c], c == 0 ? dlv[0] : dp[0]);
       fd[1][c] = load_bf16x8(dc + 8192 + (rA ^ (c << 5)));
       fence();
     }
     read_rows(1);
     fence();
-    // P2: block 1 scores; block 0 elements 0..15 (stages up to slot 15), its m = 0
+    // P2: block 1 scores; block 0 elements (stages up to slot 15), its m = 0
     // transposed operands, and the packing of its elements 0..7.
-    s[1] = f32x16{};
-    dp[1] = dlv[1];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
+      const int c = k / 2;
       if (k % 2 == 0)
-        s[1] = mfma_bf16(fq[1][k / 2], kf[k / 2], s[1]);
+        s[1] = mfma_bf16(fq[1][c], kf[c], c == 0 ? f32x16{} : s[1]);
       else
-        dp[1] = mfma_bf16(fd[1][k / 2], vf[k / 2], dp[1]);
+        dp[1] = mfma_bf16(fd[1][c], vf[c], c == 0 ? dlv[1] : dp[1]);
       elements(0, k);
       if (k < 4) read_tr(0, 0, k);
-      if (k >= 11 && k < 15) pack(0, 0, k - 11);
+      if (k >= 10 && k < 14) pack(0, 0, k - 10);
       fence();
     }
     // P3: block 0 gradients (slot 2(4m + db): dV, slot +1: dK); block 0's last
@@ -375,13 +366,13 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     for (int k = 0; k < 16; ++k) {
       const int m = k / 8, db = (k / 2) % 4;
       if (k % 2 == 0)
-        dv[db] = mfma_bf16(pf[0][m], dot[0][m][db], dv[db]);
+        mfma_acc(dv[db], pf[0][m], dot[0][m][db]);
       else
-        dk[db] = mfma_bf16(sf[0][m], qtf[0][m][db], dk[db]);
-      if (k < 3) elements(0, 16 + k);
+        mfma_acc(dk[db], sf[0][m], qtf[0][m][db]);
+      if (k < 2) elements(0, 16 + k);
       elements(1, k);
-      if (k >= 3 && k < 7) pack(0, 1, k - 3);
-      if (k >= 11 && k < 15) pack(1, 0, k - 11);
+      if (k >= 2 && k < 6) pack(0, 1, k - 2);
+      if (k >= 10 && k < 14) pack(1, 0, k - 10);
       if (k < 8 && k % 2 == 0) read_tr(0, 1, db);
       if (k >= 8 && k % 2 == 1) read_tr(1, 0, db);
       fence();
@@ -392,11 +383,11 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     for (int k = 0; k < 16; ++k) {
       const int m = k / 8, db = (k / 2) % 4;
       if (k % 2 == 0)
-        dv[db] = mfma_bf16(pf[1][m], dot[1][m][db], dv[db]);
+        mfma_acc(dv[db], pf[1][m], dot[1][m][db]);
       else
-        dk[db] = mfma_bf16(sf[1][m], qtf[1][m][db], dk[db]);
-      if (k < 3) elements(1, 16 + k);
-      if (k >= 3 && k < 7) pack(1, 1, k - 3);
+        mfma_acc(dk[db], sf[1][m], qtf[1][m][db]);
+      if (k < 2) elements(1, 16 + k);
+      if (k >= 2 && k < 6) pack(1, 1, k - 2);
       if (k < 8 && k % 2 == 0) read_tr(1, 1, db);
       fence();
     }
@@ -454,6 +445,11 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     if (it + 2 < n_iter) step(BoolTag<false>{}, it + 2, qs2, ds2, xs2, xs0, qs1, ds1, xs1);
   }
 
+  // The accumulators were last written by inline-asm MFMAs, which the compiler's
+  // hazard tracking does not see: wait out the MFMA write latency before they are read.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+               : "+a"(dk[0]), "+a"(dk[1]), "+a"(dk[2]), "+a"(dk[3]), "+a"(dv[0]), "+a"(dv[1]), "+a"(dv[2]),
+                 "+a"(dv[3]));
   // lane = d column, register i of half h = key kw + mfma32_row(i, h).  The
   // read-modify-write of dK and dV goes in groups of 16 keys x 2 tensors so that the
   // loads of a group are in flight together (the two pointers do not alias).

@@ -41,6 +41,17 @@ __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// acc += A*B with the accumulator in AGPRs (v_mfma_f32_32x32x16_bf16 in inline asm),
+// for kernels whose other MFMAs write vector registers (the compiler picks one
+// register form for all MFMAs of a function).  The compiler does not see this as
+// an MFMA, so the caller keeps its hazards in order: A and B written by vector ALU
+// instructions at least two instructions earlier, the accumulator touched only by
+// these MFMAs, and no read of it by other instructions within 20 wait states of
+// the last write.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 // Negation of 8 bf16 values (sign bits flipped: exact).
 __device__ __forceinline__ bf16x8 neg_bf16x8(bf16x8 v) {
   const u32x4 m = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
