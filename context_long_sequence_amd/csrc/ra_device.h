@@ -116,7 +116,7 @@ struct Mfma<float> {
 
 // Row of the K tile that feeds accumulator row r of a 32-key block, chosen so
 // that accumulator register i of half-wave h holds key 16h + i.
-__device__ __forceinline__ int key_of_row(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+__host__ __device__ __forceinline__ int key_of_row(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
 
 // ---- LDS tiles of 128-element bf16 rows (256 B per row, no padding) ------------------
 // The 16 chunks of 16 bytes of row r are stored XOR-swizzled at chunk position
@@ -130,15 +130,15 @@ __device__ __forceinline__ int key_of_row(int r) { return 16 * ((r >> 2) & 1) + 
 // chunk each lane fetches.
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 4) & 1); }
+__host__ __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 4) & 1); }
 
-__device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
+__host__ __device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
 
 // Byte offsets of the two MFMA operand reads of such tiles.
 //
 // Row reads (16 bytes): lane l reads chunk 2s + l/32 of row key_of_row(l % 32) (plus
 // a multiple of 32 rows); its offset is row_read_base(l) ^ (s << 5).
-__device__ __forceinline__ int row_read_base(int lane) {
+__host__ __device__ __forceinline__ int row_read_base(int lane) {
   const int r = key_of_row(lane & 31), h = lane >> 5;
   return r * 256 + 32 * (2 * (r & 3) + ((r >> 2) & 1)) + 16 * (h ^ ((r >> 4) & 1));
 }
@@ -152,7 +152,7 @@ __device__ __forceinline__ int row_read_base(int lane) {
 struct TrBases {
   int b0, b1;
 };
-__device__ __forceinline__ TrBases tr_bases(int lane) {
+__host__ __device__ __forceinline__ TrBases tr_bases(int lane) {
   const int s16 = lane & 15, mm = s16 & 3, kk = s16 >> 2, h = lane >> 5;
   const int x = 2 * ((lane >> 4) & 1) + (mm >> 1);
   const int sub8 = 8 * (mm & 1);
