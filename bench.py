@@ -10,8 +10,8 @@ all inputs resident in HBM.
 Throughput counts ALGORITHMIC flops on live (unmasked) pairs only: 4*Hq*d per pair
 forward (QK^T and PV) and 10*Hq*d backward (QK^T recomputed, dP, dV, dK, dQ).
 
-Prints ONE JSON line (rank 0).  --gpus N with N > 1 exits: this build measures one
-GPU's share.
+Prints ONE JSON line (rank 0).  --gpus N with N > 1 exits: the benchmark measures
+one GPU's share of the ring.
 """
 
 from __future__ import annotations
@@ -121,15 +121,15 @@ class Timer:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU's share of the ring (one rank); --gpus {args.gpus} is not supported "
-              "in this build: run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py measures one GPU's share of the ring (one rank); --gpus {args.gpus} is not "
+              "supported: run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
     import torch
 
     import context_long_sequence_amd as ra
-    from synthetic import CONFIGS, METRIC_CONFIG, make_workload
+    from synthetic import LLAMA3_8K_FWD, METRIC_CONFIG, PACKED16K_FWD, make_workload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -275,7 +275,7 @@ def main():
         cold_ms = float(np.median(cold))
         extra["cache_flushed"] = {"ms_per_step_median": round(cold_ms, 4),
                                   "tflops": round(flops / (cold_ms * 1e-3) / 1e12, 2), "steps": len(cold)}
-        extra.update(side_measurements(torch, ra, np, dev, CONFIGS, make_workload))
+        extra.update(side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_workload))
         zz = extra["zigzag_64k_cp8"]
         # the ring runs at the pace of its slowest rank: contiguous rank 7 (this line's
         # step) against the slower of zigzag ranks 0 and 7 (all ranks have equal work)
@@ -355,7 +355,7 @@ def packed_live_pairs(lengths, C, rank):
     return total
 
 
-def side_measurements(torch, ra, np, dev, CONFIGS, make_workload):
+def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_workload):
     """Forward TFLOP/s of the 8K and packed-16K shares, the segment-id kernel time, the
     load-balanced (zigzag) 64K forward+backward of ranks 0 and 7, the 64K ring with
     overlapped receives, the head-sharded and gathered-KV 64K shares, and the peak workspace of one forward+backward at S = 16K..128K
@@ -378,7 +378,7 @@ def side_measurements(torch, ra, np, dev, CONFIGS, make_workload):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
 
     # 8K Llama-3-8B-shaped share (rank 3 of 4), forward
-    c2 = CONFIGS[2]
+    c2 = LLAMA3_8K_FWD
     wl = make_workload(c2, q_chunks=[c2.rank])
     q, ks, vs = bf(wl.q_local), [bf(k) for k in wl.k_chunks], [bf(v) for v in wl.v_chunks]
     ws = ra.RingWorkspace(1, c2.C, c2.Hq, c2.d, dev)
@@ -387,7 +387,7 @@ def side_measurements(torch, ra, np, dev, CONFIGS, make_workload):
     out["fwd_8k_cp4_r3"] = {"ms": round(ms, 4), "tflops": round(4.0 * c2.Hq * c2.d * pairs / (ms * 1e-3) / 1e12, 2)}
 
     # packed 16K share (rank 2 of 4): segment ids + forward + backward
-    c4 = CONFIGS[4].with_(backward=True)
+    c4 = PACKED16K_FWD.with_(backward=True)
     wl = make_workload(c4, q_chunks=[c4.rank])
     q, ks, vs = bf(wl.q_local), [bf(k) for k in wl.k_chunks], [bf(v) for v in wl.v_chunks]
     do = bf(wl.do)

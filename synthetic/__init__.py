@@ -4,7 +4,12 @@ merging or gradient arithmetic lives here."""
 
 from .workloads import (  # noqa: F401
     CONFIGS,
+    CTX64K_FWD,
+    LLAMA3_8K_BWD,
+    LLAMA3_8K_FWD,
     METRIC_CONFIG,
+    PACKED16K_FWD,
+    TINY_RING,
     Workload,
     bf16_round,
     chunk_view,

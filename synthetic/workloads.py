@@ -65,16 +65,17 @@ class Config:
         return dataclasses.replace(self, **kw)
 
 
-CONFIGS = {
-    1: Config("tiny_ring_fp32_S1k_cp4_r3", 1, 1024, 4, 3, 1, 1, 64, "f32", True, False, False, 1),
-    2: Config("llama3_8b_S8k_cp4_r3_fwd", 1, 8192, 4, 3, 32, 8, 128, "bf16", True, False, False, 2),
-    3: Config("ctx64k_cp8_r7_fwd", 1, 65536, 8, 7, 32, 8, 128, "bf16", True, False, False, 3),
-    4: Config("packed16k_cp4_r2_fwd", 1, 16384, 4, 2, 32, 8, 128, "bf16", True, True, False, 4),
-    5: Config("llama3_8b_S8k_cp4_r3_bwd", 1, 8192, 4, 3, 32, 8, 128, "bf16", True, False, True, 5),
-}
+TINY_RING = Config("tiny_ring_fp32_S1k_cp4_r3", 1, 1024, 4, 3, 1, 1, 64, "f32", True, False, False, 1)
+LLAMA3_8K_FWD = Config("llama3_8b_S8k_cp4_r3_fwd", 1, 8192, 4, 3, 32, 8, 128, "bf16", True, False, False, 2)
+CTX64K_FWD = Config("ctx64k_cp8_r7_fwd", 1, 65536, 8, 7, 32, 8, 128, "bf16", True, False, False, 3)
+PACKED16K_FWD = Config("packed16k_cp4_r2_fwd", 1, 16384, 4, 2, 32, 8, 128, "bf16", True, True, False, 4)
+LLAMA3_8K_BWD = Config("llama3_8b_S8k_cp4_r3_bwd", 1, 8192, 4, 3, 32, 8, 128, "bf16", True, False, True, 5)
+
+# The five workloads by name.
+CONFIGS = {c.name: c for c in (TINY_RING, LLAMA3_8K_FWD, CTX64K_FWD, PACKED16K_FWD, LLAMA3_8K_BWD)}
 
 # The headline measurement: the 64K share, forward and backward.
-METRIC_CONFIG = CONFIGS[3].with_(name="ctx64k_cp8_r7_fwd_bwd", backward=True)
+METRIC_CONFIG = CTX64K_FWD.with_(name="ctx64k_cp8_r7_fwd_bwd", backward=True)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from synthetic import CONFIGS, METRIC_CONFIG, make_workload
+from synthetic import CONFIGS, LLAMA3_8K_BWD, METRIC_CONFIG, PACKED16K_FWD, make_workload
 from tests.gpu_util import device, lib, lse_close, max_abs, rel_to_max, report, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
@@ -43,10 +43,10 @@ def _tols(cfg):
     return (1e-4, 1e-4) if cfg.dtype == "f32" else (2e-2, 1e-3)
 
 
-@pytest.mark.parametrize("n", [1, 2, 4])
-def test_forward_config_full(n):
+@pytest.mark.parametrize("name", ["tiny_ring_fp32_S1k_cp4_r3", "llama3_8b_S8k_cp4_r3_fwd", "packed16k_cp4_r2_fwd"])
+def test_forward_config_full(name):
     ra = lib()
-    cfg = CONFIGS[n]
+    cfg = CONFIGS[name]
     wl = make_workload(cfg, q_chunks=[cfg.rank])
     q, ks, vs = _device_inputs(wl)
     seg_d, seg_ref = _seg(wl)
@@ -85,7 +85,7 @@ def test_packed_config_rank2_dead_steps_cost_nothing():
     """Packed 16K, rank 2: chunks 0 and 3 have no live pair; their steps return the merge
     identity and merging them leaves the running result bit-identical."""
     ra = lib()
-    cfg = CONFIGS[4]
+    cfg = PACKED16K_FWD
     wl = make_workload(cfg, q_chunks=[cfg.rank])
     q, ks, vs = _device_inputs(wl)
     seg_d, _ = _seg(wl)
@@ -116,7 +116,7 @@ def _grad_errors(dq, dks, dvs, dq_ref, dk_ref, dv_ref):
 
 def test_backward_config5_full():
     ra = lib()
-    cfg = CONFIGS[5]
+    cfg = LLAMA3_8K_BWD
     wl = make_workload(cfg, q_chunks=[cfg.rank])
     q, ks, vs = _device_inputs(wl)
     do = to_dev(wl.do, torch.bfloat16)
@@ -135,7 +135,7 @@ def test_backward_packed_config4_full():
     """Backward on the packed 16K share (its forward is config 4; dO drawn from the
     config's own seed stream)."""
     ra = lib()
-    cfg = CONFIGS[4].with_(backward=True)
+    cfg = PACKED16K_FWD.with_(backward=True)
     wl = make_workload(cfg, q_chunks=[cfg.rank])
     q, ks, vs = _device_inputs(wl)
     seg_d, seg_ref = _seg(wl)

@@ -29,10 +29,10 @@ def _poisoned_slots(ra, k, v):
     return sl
 
 
-@pytest.mark.parametrize("n", [5, 4])
-def test_overlapped_ring_is_bit_identical(n):
+@pytest.mark.parametrize("name", ["llama3_8b_S8k_cp4_r3_bwd", "packed16k_cp4_r2_fwd"])
+def test_overlapped_ring_is_bit_identical(name):
     ra = lib()
-    cfg = CONFIGS[n].with_(backward=True)
+    cfg = CONFIGS[name].with_(backward=True)
     wl, q, ks, vs, do = _inputs(cfg)
     seg = None
     if cfg.packed:

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from synthetic import CONFIGS, make_workload
+from synthetic import LLAMA3_8K_FWD, PACKED16K_FWD, make_workload
 from tests.gpu_util import lib, lse_close, max_abs, rel_to_max, report, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
@@ -25,8 +25,8 @@ def _seg(ra, wl):
 
 
 ULYSSES = {
-    "causal": CONFIGS[2].with_(name="ulysses_S2k_h4", S=2048, CP=1, rank=0, Hq=4, Hkv=1, backward=True, seed=21),
-    "packed": CONFIGS[4].with_(name="ulysses_packed_S4k_h4", S=4096, CP=1, rank=0, Hq=4, Hkv=1, min_len=256,
+    "causal": LLAMA3_8K_FWD.with_(name="ulysses_S2k_h4", S=2048, CP=1, rank=0, Hq=4, Hkv=1, backward=True, seed=21),
+    "packed": PACKED16K_FWD.with_(name="ulysses_packed_S4k_h4", S=4096, CP=1, rank=0, Hq=4, Hkv=1, min_len=256,
                                max_len=1024, backward=True, seed=22),
 }
 
@@ -56,8 +56,8 @@ def test_ulysses_share(case):
 
 
 GATHERED = {
-    "causal_r3": CONFIGS[2].with_(name="gathered_S4k_cp4_r3", S=4096, Hq=8, Hkv=2, backward=True, seed=31),
-    "packed_r2": CONFIGS[4].with_(name="gathered_packed_S4k_cp4_r2", S=4096, Hq=8, Hkv=2, min_len=256,
+    "causal_r3": LLAMA3_8K_FWD.with_(name="gathered_S4k_cp4_r3", S=4096, Hq=8, Hkv=2, backward=True, seed=31),
+    "packed_r2": PACKED16K_FWD.with_(name="gathered_packed_S4k_cp4_r2", S=4096, Hq=8, Hkv=2, min_len=256,
                                   max_len=1024, backward=True, seed=32),
 }
 

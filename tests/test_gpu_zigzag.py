@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from synthetic import CONFIGS, make_workload, zigzag_indices, zigzag_take
+from synthetic import LLAMA3_8K_FWD, PACKED16K_FWD, TINY_RING, make_workload, zigzag_indices, zigzag_take
 from tests.gpu_util import lib, lse_close, max_abs, rel_to_max, report, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
@@ -19,13 +19,13 @@ pytestmark = pytest.mark.gpu
 TD = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 CASES = {
-    "bf16_cp4_r0": CONFIGS[2].with_(name="zz_bf16_cp4_r0", S=4096, rank=0, Hq=8, Hkv=2, backward=True, seed=11),
-    "bf16_cp4_r3": CONFIGS[2].with_(name="zz_bf16_cp4_r3", S=4096, rank=3, Hq=8, Hkv=2, backward=True, seed=12),
-    "bf16_cp4_r2_nocausal": CONFIGS[2].with_(name="zz_bf16_cp4_r2_nc", S=2048, rank=2, Hq=4, Hkv=1, causal=False,
+    "bf16_cp4_r0": LLAMA3_8K_FWD.with_(name="zz_bf16_cp4_r0", S=4096, rank=0, Hq=8, Hkv=2, backward=True, seed=11),
+    "bf16_cp4_r3": LLAMA3_8K_FWD.with_(name="zz_bf16_cp4_r3", S=4096, rank=3, Hq=8, Hkv=2, backward=True, seed=12),
+    "bf16_cp4_r2_nocausal": LLAMA3_8K_FWD.with_(name="zz_bf16_cp4_r2_nc", S=2048, rank=2, Hq=4, Hkv=1, causal=False,
                                              backward=True, seed=13),
-    "packed_cp4_r1": CONFIGS[4].with_(name="zz_packed_cp4_r1", S=4096, rank=1, Hq=8, Hkv=2, min_len=256,
+    "packed_cp4_r1": PACKED16K_FWD.with_(name="zz_packed_cp4_r1", S=4096, rank=1, Hq=8, Hkv=2, min_len=256,
                                       max_len=1024, backward=True, seed=14),
-    "f32_d64_cp2_r1": CONFIGS[1].with_(name="zz_f32_d64_cp2_r1", S=1024, CP=2, rank=1, Hq=2, Hkv=1, backward=True,
+    "f32_d64_cp2_r1": TINY_RING.with_(name="zz_f32_d64_cp2_r1", S=1024, CP=2, rank=1, Hq=2, Hkv=1, backward=True,
                                        seed=15),
 }
 

@@ -3,7 +3,8 @@
 import numpy as np
 import torch
 
-from synthetic import CONFIGS, METRIC_CONFIG, bf16_round, draw_packed_lengths, make_workload
+from synthetic import (CONFIGS, CTX64K_FWD, LLAMA3_8K_BWD, LLAMA3_8K_FWD, METRIC_CONFIG, PACKED16K_FWD, TINY_RING,
+                       bf16_round, draw_packed_lengths, make_workload)
 
 
 def test_bf16_round_matches_torch_round_to_nearest_even():
@@ -25,7 +26,7 @@ def test_packed_lengths_cover_row_exactly():
 
 
 def test_packed_workload_position_ids_restart_per_sample():
-    wl = make_workload(CONFIGS[4])
+    wl = make_workload(PACKED16K_FWD)
     pos = wl.position_ids[0]
     starts = np.concatenate([[0], np.cumsum(wl.lengths)[:-1]])
     assert np.all(pos[starts] == 0)
@@ -34,8 +35,8 @@ def test_packed_workload_position_ids_restart_per_sample():
 
 
 def test_workloads_are_deterministic_and_bf16_exact():
-    a = make_workload(CONFIGS[2])
-    b = make_workload(CONFIGS[2], q_chunks=[3])
+    a = make_workload(LLAMA3_8K_FWD)
+    b = make_workload(LLAMA3_8K_FWD, q_chunks=[3])
     np.testing.assert_array_equal(a.q_local, b.q_local)
     np.testing.assert_array_equal(a.k_chunks[1], b.k_chunks[1])
     assert b.q_chunks[0] is None
@@ -44,8 +45,9 @@ def test_workloads_are_deterministic_and_bf16_exact():
 
 
 def test_config_shapes():
-    c = CONFIGS
-    assert (c[1].S, c[1].CP, c[1].rank, c[1].C, c[1].d, c[1].dtype) == (1024, 4, 3, 256, 64, "f32")
-    assert (c[3].S, c[3].CP, c[3].rank, c[3].C) == (65536, 8, 7, 8192)
-    assert c[5].backward and not c[2].backward
+    t, x = TINY_RING, CTX64K_FWD
+    assert (t.S, t.CP, t.rank, t.C, t.d, t.dtype) == (1024, 4, 3, 256, 64, "f32")
+    assert (x.S, x.CP, x.rank, x.C) == (65536, 8, 7, 8192)
+    assert LLAMA3_8K_BWD.backward and not LLAMA3_8K_FWD.backward
+    assert PACKED16K_FWD.packed and len(CONFIGS) == 5 and all(CONFIGS[k].name == k for k in CONFIGS)
     assert METRIC_CONFIG.backward and METRIC_CONFIG.S == 65536

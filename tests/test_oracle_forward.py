@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synthetic import CONFIGS, make_workload
+from synthetic import PACKED16K_FWD, make_workload
 from tests._brute import brute_attention
 
 
@@ -146,7 +146,7 @@ def test_packed_sample_starts_attend_only_themselves_full_size():
     """Packed 16K row, rank 2 of 4: a token with position 0 starts a sample, so under
     the causal same-sample mask it sees only itself: O_i = V_i, LSE_i = scale q_i.k_i.
     Pinned at the real size through the ring path (every chunk, every merge)."""
-    cfg = CONFIGS[4]
+    cfg = PACKED16K_FWD
     wl = make_workload(cfg)
     seg = oracle.segment_ids(wl.position_ids)
     C, r = cfg.C, cfg.rank

@@ -5,12 +5,12 @@ import numpy as np
 import pytest
 
 import oracle
-from synthetic import CONFIGS, make_workload
+from synthetic import PACKED16K_FWD, make_workload
 from tests._brute import brute_segment_ids
 
 
 def test_segment_ids_equal_generator_sample_index_full_size():
-    wl = make_workload(CONFIGS[4])
+    wl = make_workload(PACKED16K_FWD)
     seg = oracle.segment_ids(wl.position_ids)
     np.testing.assert_array_equal(seg, wl.sample_index)
     assert seg.dtype == np.int32
@@ -46,7 +46,7 @@ def test_packed_rank2_structure():
     """Samples are at most 4096 = one chunk long, so for rank 2 of the 16K row chunk 0
     never shares a sample with a local query, and chunk 3 lies in the future: two of the
     four ring steps have no live pair."""
-    cfg = CONFIGS[4]
+    cfg = PACKED16K_FWD
     wl = make_workload(cfg)
     seg = oracle.segment_ids(wl.position_ids)
     C, r = cfg.C, cfg.rank
