@@ -386,3 +386,32 @@ def test_invalid_arguments_enqueue_nothing():
         ra.ring_attn_fwd_step(q, k, k, o, lse, q_offset=64, kv_offset=0, causal=True, scale=0.1, seg_ids=seg)
     assert e.value.status == 1  # q range past seg_len
     assert torch.all(o == 0) and torch.all(lse == 0)
+
+
+@pytest.mark.parametrize("shift", [1 << 31, (1 << 40) + 12345])
+def test_steps_depend_only_on_offset_differences(shift):
+    """The causal rule compares global positions, so adding the same amount to both
+    offsets (here past 2^31, where the kernels' clamped 32-bit arithmetic must still
+    give the exact rule) changes nothing: forward and backward outputs bit-identical."""
+    ra = lib()
+    rng = np.random.default_rng(77)
+    B, Sq, Sk, Hq, Hkv, d = 1, 300, 260, 4, 2, 128
+    q, k, v = _qkv(rng, B, Sq, Sk, Hq, Hkv, d, "bf16")
+    do = bf16_round(rng.standard_normal((B, Sq, Hq, d), dtype=np.float32))
+    qd, kd, vd, dod = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+    lse_f = to_dev(rng.uniform(4.0, 6.0, (B, Hq, Sq)).astype(np.float32), torch.float32)
+    delta = to_dev(0.1 * rng.standard_normal((B, Hq, Sq), dtype=np.float32), torch.float32)
+    outs = []
+    for base in (0, shift):
+        o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=device())
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=device())
+        ra.ring_attn_fwd_step(qd, kd, vd, o, lse, q_offset=base + 200, kv_offset=base + 100, causal=True,
+                              scale=0.088)
+        dq = torch.zeros((B, Sq, Hq, d), dtype=torch.float32, device=device())
+        dk = torch.zeros((B, Sk, Hkv, d), dtype=torch.float32, device=device())
+        dv = torch.zeros_like(dk)
+        ra.ring_attn_bwd_step(qd, kd, vd, dod, lse_f, delta, dq, dk, dv, q_offset=base + 200, kv_offset=base + 100,
+                              causal=True, scale=0.088)
+        outs.append([t.cpu().numpy() for t in (o, lse, dq, dk, dv)])
+    for a_, b_ in zip(outs[0], outs[1]):
+        assert np.array_equal(a_, b_)
