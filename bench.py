@@ -567,23 +567,53 @@ def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_wor
 
 
 def cpu_baseline(cfg, wl=None):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload: forward
-    and backward of the last R query rows of the 64K share (each sees all 65536 keys),
-    all 32 heads.  Reported in the metric's unit on the sample's algorithmic flops."""
+    """The fp64 oracle, as it stands, timed on the host cores (one query head per
+    worker thread, single-threaded BLAS per worker; heads are independent).
+
+    `value`: forward + backward of a bounded sample of the benchmark's workload, the
+    last R query rows of the 64K share (each sees all 65536 keys), all 32 heads, in
+    the metric's unit on the sample's algorithmic flops.  `per_config_s`: wall time of
+    the oracle on each of the five workloads at full size (ring forward, plus the
+    ring backward for the 8K backward workload); the 64K forward and the benchmark's
+    64K forward + backward are extrapolated from the sample by live pairs (each row
+    of the sample sees at least as many keys as an average row) and labelled so."""
     import numpy as np
 
     import oracle
-    from synthetic import make_workload
+    from oracle import parallel as opar
+    from synthetic import CONFIGS, LLAMA3_8K_BWD, LLAMA3_8K_FWD, PACKED16K_FWD, TINY_RING, make_workload
 
-    blas = "unknown"
-    try:
-        from threadpoolctl import threadpool_info
-        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        threads = max([i.get("num_threads", 1) for i in infos] or [1])
-        if infos:
-            blas = f"{infos[0].get('internal_api', '?')} {infos[0].get('version', '')}".strip()
-    except Exception:  # noqa: BLE001
-        threads = 1
+    workers = opar.host_cores()
+    per_cfg = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    # tiny fp32 ring (one head): the plain call
+    w1 = make_workload(TINY_RING, q_chunks=[TINY_RING.rank])
+    per_cfg[TINY_RING.name] = round(timed(lambda: oracle.ring_forward(
+        w1.q_local, w1.k_chunks, w1.v_chunks, TINY_RING.rank, TINY_RING.CP, TINY_RING.scale, True)), 3)
+    # 8K forward and packed 16K forward: the ring forward per head
+    for c in (LLAMA3_8K_FWD, PACKED16K_FWD):
+        w = make_workload(c, q_chunks=[c.rank])
+        seg = oracle.segment_ids(w.position_ids) if c.packed else None
+        per_cfg[c.name] = round(timed(lambda: opar.ring_forward_heads(
+            w.q_local, w.k_chunks, w.v_chunks, c.rank, c.CP, c.scale, True, seg, workers=workers)), 3)
+    # 8K backward: ring forward (for O, LSE) + ring backward
+    c5 = LLAMA3_8K_BWD
+    w5 = make_workload(c5, q_chunks=[c5.rank])
+
+    def fb5():
+        o, lse = opar.ring_forward_heads(w5.q_local, w5.k_chunks, w5.v_chunks, c5.rank, c5.CP, c5.scale, True,
+                                         workers=workers)
+        opar.ring_backward_heads(w5.q_local, w5.k_chunks, w5.v_chunks, o, lse, w5.do, c5.rank, c5.CP, c5.scale,
+                                 True, workers=workers)
+
+    per_cfg[c5.name] = round(timed(fb5), 3)
+
+    # the bounded sample of the benchmark's 64K workload
     if wl is None:
         wl = make_workload(cfg, q_chunks=[cfg.rank])
     C, r = cfg.C, cfg.rank
@@ -594,17 +624,33 @@ def cpu_baseline(cfg, wl=None):
     k_full, v_full = wl.k_full(), wl.v_full()
     q_idx = r * C + rows
     k_idx = np.arange(cfg.S)
-    t0 = time.perf_counter()
-    o_ref, l_ref = oracle.attention_full(q_rows, k_full, v_full, q_idx, k_idx, cfg.scale, True)
-    delta = oracle.bwd_delta(o_ref, do_rows)
-    oracle.attention_bwd_full(q_rows, k_full, v_full, do_rows, l_ref, delta, q_idx, k_idx, cfg.scale, True)
-    dt = time.perf_counter() - t0
+    res = {}
+
+    def fwd():
+        res["o"], res["lse"] = opar.attention_full_heads(q_rows, k_full, v_full, q_idx, k_idx, cfg.scale, True,
+                                                         workers=workers)
+
+    def bwd():
+        delta = oracle.bwd_delta(res["o"], do_rows)
+        opar.attention_bwd_full_heads(q_rows, k_full, v_full, do_rows, res["lse"], delta, q_idx, k_idx, cfg.scale,
+                                      True, workers=workers)
+
+    t_f = timed(fwd)
+    t_b = timed(bwd)
+    dt = t_f + t_b
     pairs = int(np.sum(q_idx + 1))
     flops = 14.0 * cfg.Hq * cfg.d * pairs
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    all_pairs = live_pairs_causal(C, r)
+    c3 = CONFIGS["ctx64k_cp8_r7_fwd"]
+    per_cfg[c3.name + " (extrapolated from the sample)"] = round(t_f * all_pairs / pairs, 1)
+    per_cfg[cfg.name + " (extrapolated from the sample)"] = round(dt * all_pairs / pairs, 1)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
+            "affinity_cores": opar.affinity_cores(), "blas": opar.blas_info(),
+            "per_config_s": per_cfg,
             "sample": f"fp64 numpy oracle fwd+bwd of the last {R} query rows of the 64K share "
                       f"(rank 7, all {cfg.Hq} heads, {cfg.S} keys each): {pairs} live pairs, "
-                      f"{flops:.3e} algorithmic flop in {dt:.1f} s; numpy BLAS: {blas}"}
+                      f"{flops:.3e} algorithmic flop in {dt:.1f} s (fwd {t_f:.1f} s, bwd {t_b:.1f} s) on "
+                      f"{workers} worker threads, one query head each, single-threaded {opar.blas_info()} BLAS"}
 
 
 if __name__ == "__main__":

@@ -4,10 +4,6 @@
 #include "ra_device.h"
 #include "ra_host.h"
 
-#ifndef RA_DKDV_WAVES
-#define RA_DKDV_WAVES 4  // waves (x 32 keys) per dK/dV workgroup of the bf16 d=128 path
-#endif
-
 namespace ra {
 
 struct BwdArgs {

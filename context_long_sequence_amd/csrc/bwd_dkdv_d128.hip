@@ -485,7 +485,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
 }  // namespace
 
 ra_status launch_dkdv_d128(BwdArgs args, hipStream_t stream) {
-  constexpr int NW = RA_DKDV_WAVES;
+  constexpr int NW = 4;  // waves (x 32 keys) per workgroup
   args.n_tiles = (args.Sk + 32 * NW - 1) / (32 * NW);
   const int64_t n_wg = (int64_t)args.B * args.Hkv * args.n_tiles;
   if (n_wg > INT32_MAX) return fail(RA_ERR_INVALID_ARGUMENT, "too many workgroups");

@@ -16,10 +16,7 @@ constexpr int kTile = kD128Tile;
 // ------------------------------------------------------------------------------------
 // dQ: 4 waves x 32 queries of one query head; walks the key tiles of the chunk.
 // ------------------------------------------------------------------------------------
-#ifndef RA_DQ_WAVES
-#define RA_DQ_WAVES 4  // waves (x 32 queries) per dQ workgroup: 4 or 8
-#endif
-constexpr int kDqWaves = RA_DQ_WAVES;
+constexpr int kDqWaves = 4;  // waves (x 32 queries) per workgroup
 static_assert(kDqWaves == 4 || kDqWaves == 8, "a 32-row tile is 8 blocks of 1 KiB, split evenly over the waves");
 constexpr int kDqBlocks = 8 / kDqWaves;  // 1 KiB blocks of a tile copied by each wave
 constexpr int kDqThreads = 64 * kDqWaves;

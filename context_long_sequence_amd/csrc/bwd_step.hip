@@ -509,9 +509,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
 
 template <typename T, int D>
 ra_status launch_bwd(BwdArgs args, hipStream_t stream) {
-#ifndef RA_BWD_GENERIC_ONLY
   if constexpr (std::is_same<T, __bf16>::value && D == 128) return launch_bwd_d128(args, stream);
-#endif
   // dK/dV: one workgroup per (b, kv head, 128-key tile).
   args.n_tiles = (args.Sk + 32 * kWaves - 1) / (32 * kWaves);
   int64_t n_wg = (int64_t)args.B * args.Hkv * args.n_tiles;

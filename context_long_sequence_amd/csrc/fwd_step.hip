@@ -25,10 +25,6 @@
 #include <type_traits>
 
 #include "ra_device.h"
-
-#ifndef RA_FWD_BATCH
-#define RA_FWD_BATCH 1  // issue each MFMA chain's operand reads before its first MFMA
-#endif
 #include "ra_host.h"
 
 namespace ra {
@@ -397,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a) {
 
   // ---- epilogue ---------------------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const bool live = l_tot > 0.0f;
+  const bool live = l_tot != 0.0f;  // l_tot >= 0; NaN (from NaN inputs) stays live and propagates
   const float inv = live ? 1.0f / l_tot : 0.0f;
   if (q_valid) fwd_epilogue<DB>(a, oacc, inv, live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY, b, hq, qi, half);
 }
@@ -714,7 +710,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
   }
 
   const float l_tot = half_sum(l_run);
-  const bool live = l_tot > 0.0f;
+  const bool live = l_tot != 0.0f;  // l_tot >= 0; NaN (from NaN inputs) stays live and propagates
   const float inv = live ? 1.0f / l_tot : 0.0f;
   if (qv) fwd_epilogue<4>(a, oacc, inv, live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY, b, hq, qi, half);
 }

@@ -37,13 +37,23 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(int Sq, int Hq, int
       if (mw.live) {
         o = merge_o(o, reinterpret_cast<const f32x4*>(o_step)[base4 + t], mw);
         acc4[t] = o;
-        if (t - h * d4 == 0) lse_acc[li] = mw.lse;
       }
     }
     if constexpr (kOut == 1) {
       reinterpret_cast<f32x4*>(o_out)[base4 + t] = o;
     } else if constexpr (kOut == 2) {
       reinterpret_cast<bf16x4*>(o_out)[base4 + t] = to_bf16x4(o);
+    }
+  }
+  if constexpr (kMerge) {
+    // The merged LSE is written only after every thread of the row has read the
+    // running one: a head's d/4 vectors may span two waves or two passes of the loop
+    // above.
+    __syncthreads();
+    for (int h = threadIdx.x; h < Hq; h += kThreads) {
+      const int64_t li = ((int64_t)b * Hq + h) * Sq + i;
+      const MergeWeights mw = merge_weights(lse_acc[li], lse_step[li]);
+      if (mw.live) lse_acc[li] = mw.lse;
     }
   }
 }

@@ -203,7 +203,10 @@ struct MergeWeights {
 };
 __device__ __forceinline__ MergeWeights merge_weights(float L, float Ls) {
   MergeWeights r;
-  const float m = fmaxf(L, Ls);
+  // fmaxf drops a NaN operand; a NaN log-sum-exp (NaN inputs) must reach the result
+  // instead of being taken for the identity when the other side is -inf.
+  const bool nan_in = __builtin_isnan(L) || __builtin_isnan(Ls);
+  const float m = nan_in ? __builtin_nanf("") : fmaxf(L, Ls);
   r.live = m != -INFINITY;
   if (!r.live) {
     r.w = r.ws = r.inv = 0.0f;

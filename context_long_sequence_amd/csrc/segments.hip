@@ -25,12 +25,13 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(int S, const int32_t*
   int32_t* srow = seg + (int64_t)b * S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int carry = 0;
-  for (int base = 0; base < S; base += kThreads * kPer) {
+  // 64-bit token indices: base + kThreads * kPer may pass 2^31 - 1 near the S limit.
+  for (int64_t base = 0; base < S; base += kThreads * kPer) {
     int c[kPer];
     int run = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int t = base + tid * kPer + e;
+      const int64_t t = base + tid * kPer + e;
       run += (t < S && prow[t] == 0) ? 1 : 0;
       c[e] = run;
     }
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(int S, const int32_t*
     const int before = carry + wave_pre[wave] + (x - run);
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int t = base + tid * kPer + e;
+      const int64_t t = base + tid * kPer + e;
       if (t < S) srow[t] = before + c[e] - 1;
     }
     carry += wave_pre[kThreads / 64 - 1] + wave_tot[kThreads / 64 - 1];

@@ -11,6 +11,7 @@ arithmetic runs in the HIP library.
 
 from __future__ import annotations
 
+import functools
 import math
 from typing import List, Optional, Sequence, Tuple
 
@@ -26,6 +27,36 @@ def ring_schedule(rank: int, cp: int) -> List[int]:
 
 def _scale(d: int, scale: Optional[float]) -> float:
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def _torch_stream(stream) -> torch.cuda.Stream:
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _on_stream(fn):
+    """Runs `fn` with its `stream` argument as torch's current stream, so that the
+    temporaries it allocates (and the fills that zero them) belong to the stream its
+    kernels run on: the caching allocator then never hands their memory to other
+    work while those kernels may still use it."""
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kw):
+        with torch.cuda.stream(_torch_stream(kw.get("stream"))):
+            return fn(*args, **kw)
+
+    return wrapper
+
+
+def _used_on(stream: torch.cuda.Stream, tensors) -> None:
+    """Marks tensors that kernels on a second stream use, so that freeing them waits
+    for that stream's work as well."""
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
 
 
 class RingWorkspace:
@@ -65,6 +96,7 @@ def _fold_step(q, kc, vc, o_acc, lse_acc, first: bool, last: bool, out, *, q_off
             step_hook("fwd_step", step)
 
 
+@_on_stream
 def ring_forward(q_local: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chunks: Sequence[torch.Tensor],
                  rank: int, cp: int, *, causal: bool = True, scale: Optional[float] = None,
                  seg_ids: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
@@ -93,6 +125,7 @@ def ring_forward(q_local: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chun
     return out, lse
 
 
+@_on_stream
 def ring_backward(q_local: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chunks: Sequence[torch.Tensor],
                   o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor, rank: int, cp: int, *,
                   causal: bool = True, scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
@@ -178,6 +211,7 @@ def _half(t: torch.Tensor, j: int, h: int) -> torch.Tensor:
     return t[:, j * h:(j + 1) * h]
 
 
+@_on_stream
 def ring_forward_zigzag(q_local: torch.Tensor, k_ranks: Sequence[torch.Tensor], v_ranks: Sequence[torch.Tensor],
                         rank: int, cp: int, *, causal: bool = True, scale: Optional[float] = None,
                         seg_ids: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
@@ -219,6 +253,7 @@ def ring_forward_zigzag(q_local: torch.Tensor, k_ranks: Sequence[torch.Tensor], 
     return out, lse
 
 
+@_on_stream
 def ring_backward_zigzag(q_local: torch.Tensor, k_ranks: Sequence[torch.Tensor], v_ranks: Sequence[torch.Tensor],
                          o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor, rank: int, cp: int, *,
                          causal: bool = True, scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
@@ -295,6 +330,7 @@ def _streams(stream, comm_stream, device):
     return compute, comm
 
 
+@_on_stream
 def ring_forward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Tensor],
                             v_chunks: Sequence[torch.Tensor], rank: int, cp: int, *, causal: bool = True,
                             scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
@@ -309,6 +345,8 @@ def ring_forward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Tens
     compute, comm = _streams(stream, comm_stream, dev)
     ws = workspace or RingWorkspace(B, C, Hq, d, dev)
     sl = slots or RingSlots(k_chunks[0], v_chunks[0])
+    if slots is None:
+        _used_on(comm, sl.k + sl.v)
     if out is None:
         out = torch.empty_like(q_local)
     if lse is None:
@@ -344,6 +382,7 @@ def ring_forward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Tens
     return out, lse
 
 
+@_on_stream
 def ring_backward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Tensor],
                              v_chunks: Sequence[torch.Tensor], o: torch.Tensor, lse: torch.Tensor,
                              d_o: torch.Tensor, rank: int, cp: int, *, causal: bool = True,
@@ -363,6 +402,7 @@ def ring_backward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Ten
     sl = slots or RingSlots(k_chunks[0], v_chunks[0], backward=True)
     if sl.dk is None:
         raise ValueError("the backward needs slots with dK/dV buffers")
+    dk_given, dv_given = dk_chunks, dv_chunks
     if dq is None:
         dq = torch.zeros((B, C, Hq, d), dtype=torch.float32, device=dev)
     if dk_chunks is None:
@@ -371,6 +411,11 @@ def ring_backward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Ten
         dv_chunks = [torch.zeros(v.shape, dtype=torch.float32, device=dev) for v in v_chunks]
     if delta is None:
         delta = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
+    if slots is None:
+        _used_on(comm, sl.k + sl.v + sl.dk + sl.dv)
+    for given, made in ((dk_given, dk_chunks), (dv_given, dv_chunks)):
+        if given is None:
+            _used_on(comm, made)
     sched = ring_schedule(rank, cp)
     comm.wait_stream(compute)
     _lib.ring_attn_bwd_preprocess(o, d_o, delta, stream=compute)
@@ -415,6 +460,7 @@ def ring_backward_overlapped(q_local: torch.Tensor, k_chunks: Sequence[torch.Ten
 # attention over the full row: one forward step call and one backward step call
 # with offsets 0 — the same kernels at a different shape, no merges.
 
+@_on_stream
 def ulysses_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True,
                     scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -436,6 +482,7 @@ def ulysses_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal
     return out, lse
 
 
+@_on_stream
 def ulysses_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
                      d_o: torch.Tensor, *, causal: bool = True, scale: Optional[float] = None,
                      seg_ids: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
@@ -470,6 +517,7 @@ def ulysses_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
 # Hkv, d] buffer; the backward's reduce-scatter returns each chunk's dK/dV rows to
 # the chunk accumulators the same way.
 
+@_on_stream
 def gather_kv(k_chunks: Sequence[torch.Tensor], v_chunks: Sequence[torch.Tensor],
               k_all: Optional[torch.Tensor] = None, v_all: Optional[torch.Tensor] = None, stream=None):
     """Concatenate the chunks along the row into k_all/v_all [B, S, Hkv, d] (batch 1: the
@@ -488,6 +536,7 @@ def gather_kv(k_chunks: Sequence[torch.Tensor], v_chunks: Sequence[torch.Tensor]
     return k_all, v_all
 
 
+@_on_stream
 def gathered_forward(q_local: torch.Tensor, k_all: torch.Tensor, v_all: torch.Tensor, rank: int, *,
                      causal: bool = True, scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -509,6 +558,7 @@ def gathered_forward(q_local: torch.Tensor, k_all: torch.Tensor, v_all: torch.Te
     return out, lse
 
 
+@_on_stream
 def gathered_backward(q_local: torch.Tensor, k_all: torch.Tensor, v_all: torch.Tensor, o: torch.Tensor,
                       lse: torch.Tensor, d_o: torch.Tensor, rank: int, *, causal: bool = True,
                       scale: Optional[float] = None, seg_ids: Optional[torch.Tensor] = None,
@@ -534,6 +584,7 @@ def gathered_backward(q_local: torch.Tensor, k_all: torch.Tensor, v_all: torch.T
     return dq, dk_all, dv_all
 
 
+@_on_stream
 def scatter_dkv(dk_all: torch.Tensor, dv_all: torch.Tensor, dk_chunks: Sequence[torch.Tensor],
                 dv_chunks: Sequence[torch.Tensor], stream=None) -> None:
     """Copy row block c of the gathered-row gradients into the chunk accumulators

@@ -75,6 +75,13 @@ typedef struct {
 /*
  * ring_attn_fwd_step — partial attention of the local queries against one KV
  * chunk (one ring step).
+ * Defining passages: every query must see every key, and under context
+ * parallelism K/V chunks rotate around a ring so that a rank sees one chunk per
+ * step (aicassindra "Transformer math: SP math", section "Context parallelism is
+ * the axis that is independent"); the step never stores the score matrix of the
+ * chunk (archcrux, "sequence-parallel long-context attention OOM").  The
+ * softmax(scale q.k) form is the standard definition, which the pages name but do
+ * not print.
  *
  * Computes, per (b, h, i), over the visible keys j of this chunk:
  *   s_ij = softmax_scale * q_i . k_j,  LSE_i = ln sum_j exp(s_ij),
@@ -99,7 +106,11 @@ ra_status ring_attn_fwd_step(const ra_shape* shape, const void* q, const void* k
                              float* lse_step, void* stream);
 
 /*
- * lse_merge — fold one step's partial result into the running result, in place:
+ * lse_merge — fold one step's partial result into the running result, in place.
+ * Defining passage: the ranks' partial results are combined as they pass around
+ * the ring (axolotl docs "Sequence Parallelism", introduction).  The pages do not
+ * print the rule; the log-sum-exp merge below is the exact combination of two
+ * softmax partials over disjoint key sets:
  *   M = max(L, L_s);  L' = M + ln(e^(L-M) + e^(L_s-M));
  *   O' = e^(L-L') O + e^(L_s-L') O_s;   rows where both L and L_s are -inf are
  *   left unchanged.
@@ -140,7 +151,11 @@ ra_status ring_attn_fwd_step_merge(const ra_shape* shape, const void* q, const v
                                    void* o_out, int32_t out_dtype, void* stream);
 
 /*
- * segment_mask_from_pos — sample (segment) id of every token of packed rows:
+ * segment_mask_from_pos — sample (segment) id of every token of packed rows.
+ * Defining passages: axolotl docs "Sequence Parallelism", section Mamba/SSM Hybrid
+ * Models (sample ids derived from position_ids by a cumulative sum that stays
+ * correct across chunk boundaries) and section Sample Packing with Sequence
+ * Parallelism (samples are packed before the row is split):
  *   seg_ids[b, t] = #{t' <= t : position_ids[b, t'] == 0} - 1,
  * computed over the GLOBAL row so that a context-parallel chunk that starts in
  * the middle of a sample keeps that sample's id.  Tokens before the first zero
@@ -154,6 +169,11 @@ ra_status segment_mask_from_pos(int32_t batch, int64_t seq_len, const int32_t* p
 /*
  * ring_attn_bwd_preprocess — delta[b, h, i] = sum_d dO[b, i, h, :] * O[b, i, h, :]
  * (fp32 accumulation), the per-row term of the softmax gradient.
+ * The pages do not describe this step; it belongs to the closed-form gradient of
+ * softmax attention that the backward recomputes (archcrux, "sequence-parallel
+ * long-context attention OOM": the backward still runs over the whole context),
+ * and is computed once per backward from the forward's returned O, before the
+ * ring steps.
  * o, d_o [B, Sq, Hq, d] in dtype;  delta [B, Hq, Sq] fp32 out.
  * Errors: as lse_merge; RA_ERR_UNSUPPORTED for d not in {64, 128}.
  */
@@ -163,6 +183,12 @@ ra_status ring_attn_bwd_preprocess(int32_t batch, int32_t q_len, int32_t heads_q
 
 /*
  * ring_attn_bwd_step — one ring step of the backward pass for one KV chunk.
+ * Defining passages: archcrux, "sequence-parallel long-context attention OOM"
+ * (FlashAttention-style kernels avoid the score matrix but still backpropagate
+ * over the whole context; recomputing it trades compute for memory), with the
+ * ring order of aicassindra "Transformer math: SP math", section "Context
+ * parallelism is the axis that is independent".  The gradient formulas are the
+ * closed form of softmax attention (not printed on the pages).
  * With the FINAL merged lse of the forward and delta from the preprocess:
  *   P_ij = exp(s_ij - LSE_i) on visible pairs (0 elsewhere), s as in the forward;
  *   dV_j += sum_i P_ij dO_i;  dP_ij = dO_i . v_j;  dS_ij = P_ij (dP_ij - delta_i);

@@ -53,7 +53,10 @@ def test_segment_mask_from_pos_bit_exact(B, S, lo, hi, mid):
 
 # ---- merge -----------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("B,Sq,Hq,d", [(1, 300, 4, 128), (2, 77, 3, 64), (1, 5, 1, 4)])
+# (1, 9, 100, 12): a head's 3 vectors straddle waves and passes of the per-row loop
+# (300 vectors per row > 256 threads), so the running LSE must be read by every
+# thread of a head before it is overwritten.
+@pytest.mark.parametrize("B,Sq,Hq,d", [(1, 300, 4, 128), (2, 77, 3, 64), (1, 5, 1, 4), (1, 9, 100, 12)])
 def test_lse_merge(B, Sq, Hq, d):
     ra = lib()
     rng = np.random.default_rng(Sq)

@@ -1,7 +1,8 @@
 """The overlapped ring (receives of the next chunk on a second stream, two receive
 slots, event ordering) must give bit-identical results to the ring over resident
-chunks: same kernels, same order.  The receive slots start filled with NaN, so a
-step that read a slot before its copy landed would show."""
+chunks (same kernels, same order) and match the fp64 oracle.  The receive slots
+start filled with NaN, so a step that read a slot before its copy landed would
+show."""
 
 import numpy as np
 import pytest
@@ -59,3 +60,41 @@ def test_overlapped_ring_is_bit_identical(name):
     for c in range(cfg.CP):
         assert torch.equal(dk_a[c], dk_b[c]) and torch.equal(dv_a[c], dv_b[c]), c
     assert not any(bool(torch.isnan(x).any()) for x in [o_b.float(), dq_b] + dk_b + dv_b)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_S8k_cp4_r3_bwd", "packed16k_cp4_r2_fwd"])
+def test_overlapped_ring_matches_oracle(name):
+    """The overlapped ring's O, LSE and gradients (fresh zero accumulators) against the
+    fp64 oracle's ring forward and backward on the same inputs: O <= 2e-2 max-abs and
+    relative to max|O|, LSE <= 1e-3, dQ/dK/dV <= 3e-2 relative to max."""
+    import oracle
+    from oracle import parallel as opar
+    from tests.gpu_util import lse_close, max_abs, rel_to_max, report, to_np
+
+    ra = lib()
+    cfg = CONFIGS[name].with_(backward=True)
+    wl, q, ks, vs, do = _inputs(cfg)
+    seg, seg_ref = None, None
+    if cfg.packed:
+        pos = to_dev(wl.position_ids, torch.int32)
+        seg = torch.empty_like(pos)
+        ra.segment_mask_from_pos(pos, seg)
+        seg_ref = oracle.segment_ids(wl.position_ids)
+    sl = _poisoned_slots(ra, ks[0], vs[0])
+    o, lse = ra.ring_forward_overlapped(q, ks, vs, cfg.rank, cfg.CP, causal=True, seg_ids=seg, slots=sl)
+    dq, dks, dvs = ra.ring_backward_overlapped(q, ks, vs, o, lse, do, cfg.rank, cfg.CP, causal=True, seg_ids=seg,
+                                               slots=sl)
+    torch.cuda.synchronize()
+    o_ref, l_ref = opar.ring_forward_heads(wl.q_local, wl.k_chunks, wl.v_chunks, cfg.rank, cfg.CP, cfg.scale, True,
+                                           seg_ref)
+    dq_ref, dk_ref, dv_ref = opar.ring_backward_heads(wl.q_local, wl.k_chunks, wl.v_chunks, o_ref, l_ref, wl.do,
+                                                      cfg.rank, cfg.CP, cfg.scale, True, seg_ref)
+    on = to_np(o)
+    err_o, rel_o = max_abs(on, o_ref), rel_to_max(on, o_ref)
+    err_l = lse_close(to_np(lse), l_ref, 1e-3)
+    e_dq = rel_to_max(to_np(dq), dq_ref)
+    e_dk = rel_to_max(np.concatenate([to_np(x) for x in dks], 1), np.concatenate(dk_ref, 1))
+    e_dv = rel_to_max(np.concatenate([to_np(x) for x in dvs], 1), np.concatenate(dv_ref, 1))
+    report(cfg.name + "/overlapped", o_maxabs=err_o, o_rel=rel_o, lse_maxabs=err_l, dq=e_dq, dk=e_dk, dv=e_dv)
+    assert err_o <= 2e-2 and rel_o <= 2e-2
+    assert max(e_dq, e_dk, e_dv) <= 3e-2, (e_dq, e_dk, e_dv)

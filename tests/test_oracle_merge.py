@@ -1,6 +1,7 @@
 """Pins of the oracle's log-sum-exp merge (CPU only): a hand-derived worked example,
 the merge's identity, order independence and associativity."""
 
+import ast
 import itertools
 import json
 import math
@@ -14,46 +15,91 @@ import oracle
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "three_keys_hand.json")
 
 
-def _three_keys():
-    q = np.array([[[[1.0, 0.0]], [[1.0, 0.0]]]])                     # [1, 2, 1, 2]
-    k = np.array([[[[math.log(j + 1), 0.0]] for j in range(3)]])       # [1, 3, 1, 2]
-    v = np.array([[[[0.0, 1.0]], [[1.0, 1.0]], [[2.0, 1.0]]]])
+def _expr(x):
+    """Value of one fixture entry: a number, or an arithmetic expression over numbers
+    with + - * / and ln() (evaluated exactly as written, nothing else is accepted)."""
+    if isinstance(x, (int, float)):
+        return float(x)
+    node = ast.parse(x, mode="eval").body
+
+    def ev(n):
+        if isinstance(n, ast.Constant) and isinstance(n.value, (int, float)):
+            return float(n.value)
+        if isinstance(n, ast.UnaryOp) and isinstance(n.op, ast.USub):
+            return -ev(n.operand)
+        if isinstance(n, ast.BinOp) and isinstance(n.op, (ast.Add, ast.Sub, ast.Mult, ast.Div)):
+            a, b = ev(n.left), ev(n.right)
+            return {ast.Add: a + b, ast.Sub: a - b, ast.Mult: a * b, ast.Div: a / b if b else math.nan}[type(n.op)]
+        if (isinstance(n, ast.Call) and isinstance(n.func, ast.Name) and n.func.id == "ln" and len(n.args) == 1
+                and not n.keywords):
+            return math.log(ev(n.args[0]))
+        raise ValueError(f"unsupported fixture expression {x!r}")
+
+    return ev(node)
+
+
+def _arr(x):
+    return np.vectorize(_expr, otypes=[np.float64])(np.asarray(x, dtype=object))
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _three_keys(g):
+    """q [1, 2, 1, 2], k/v [1, 3, 1, 2] of the fixture (one batch row, one head)."""
+    q = _arr(g["q"])[None, :, None, :]
+    k = _arr(g["k"])[None, :, None, :]
+    v = _arr(g["v"])[None, :, None, :]
     return q, k, v
 
 
+def test_golden_expressions_parse_as_numbers():
+    assert _expr("ln(3)/3 - ln(2)/9") == pytest.approx(math.log(3) / 3 - math.log(2) / 9, abs=1e-16)
+    assert _expr("-2/9") == pytest.approx(-2 / 9, abs=1e-16)
+    with pytest.raises(ValueError):
+        _expr("__import__('os')")
+
+
 def test_hand_derived_three_key_example():
-    with open(GOLDEN) as f:
-        g = json.load(f)
-    assert g["causal"] and g["scale"] == 1.0
-    q, k, v = _three_keys()
-    o, lse = oracle.attention_full(q, k, v, np.array([2, 1]), np.arange(3), 1.0, True)
-    np.testing.assert_allclose(o[0, 0, 0], [4 / 3, 1.0], atol=1e-15)
-    np.testing.assert_allclose(o[0, 1, 0], [2 / 3, 1.0], atol=1e-15)
-    assert abs(lse[0, 0, 0] - math.log(6)) < 1e-15
-    assert abs(lse[0, 0, 1] - math.log(3)) < 1e-15
-    # chunks {0,1} and {2} of query 2, then the merge
+    g = _golden()
+    ex = g["expected"]
+    q, k, v = _three_keys(g)
+    scale, causal = float(g["scale"]), bool(g["causal"])
+    q_idx, k_idx = np.asarray(g["q_idx"]), np.asarray(g["k_idx"])
+    o, lse = oracle.attention_full(q, k, v, q_idx, k_idx, scale, causal)
+    np.testing.assert_allclose(o[0, :, 0], _arr(ex["forward"]["O"]), atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0], _arr(ex["forward"]["LSE"]), atol=1e-15)
+    # row 0 against each key chunk on its own, then the merge of the two partials
     qa = q[:, :1]
-    o01, l01 = oracle.attention_full(qa, k[:, :2], v[:, :2], np.array([2]), np.arange(2), 1.0, True)
-    o2, l2 = oracle.attention_full(qa, k[:, 2:], v[:, 2:], np.array([2]), np.array([2]), 1.0, True)
-    np.testing.assert_allclose(o01[0, 0, 0], [2 / 3, 1.0], atol=1e-15)
-    np.testing.assert_allclose(o2[0, 0, 0], [2.0, 1.0], atol=1e-15)
-    assert abs(l01[0, 0, 0] - math.log(3)) < 1e-15 and abs(l2[0, 0, 0] - math.log(3)) < 1e-15
-    om, lm = oracle.lse_merge(o01, l01, o2, l2)
-    np.testing.assert_allclose(om[0, 0, 0], [4 / 3, 1.0], atol=1e-15)
-    assert abs(lm[0, 0, 0] - math.log(6)) < 1e-15
+    parts = []
+    for ch in ex["row0_chunks"]:
+        keys = np.asarray(ch["keys"])
+        oc, lc = oracle.attention_full(qa, k[:, keys], v[:, keys], q_idx[:1], k_idx[keys], scale, causal)
+        np.testing.assert_allclose(oc[0, 0, 0], _arr(ch["O"]), atol=1e-15)
+        assert abs(lc[0, 0, 0] - _expr(ch["LSE"])) < 1e-15
+        parts.append((oc, lc))
+    om, lm = oracle.lse_merge(parts[0][0], parts[0][1], parts[1][0], parts[1][1])
+    np.testing.assert_allclose(om[0, 0, 0], _arr(ex["row0_merge"]["O"]), atol=1e-15)
+    assert abs(lm[0, 0, 0] - _expr(ex["row0_merge"]["LSE"])) < 1e-15
 
 
 def test_hand_derived_three_key_backward():
-    q, k, v = _three_keys()
+    g = _golden()
+    bw = g["expected"]["row0_backward"]
+    q, k, v = _three_keys(g)
+    scale, causal = float(g["scale"]), bool(g["causal"])
+    q_idx, k_idx = np.asarray(g["q_idx"])[:1], np.asarray(g["k_idx"])
     qa = q[:, :1]
-    o, lse = oracle.attention_full(qa, k, v, np.array([2]), np.arange(3), 1.0, True)
-    do = np.array([[[[1.0, 0.0]]]])
+    o, lse = oracle.attention_full(qa, k, v, q_idx, k_idx, scale, causal)
+    do = _arr(bw["dO"])[None, None, None, :]
     delta = oracle.bwd_delta(o, do)
-    assert abs(delta[0, 0, 0] - 4 / 3) < 1e-15
-    dq, dk, dv = oracle.attention_bwd_full(qa, k, v, do, lse, delta, np.array([2]), np.arange(3), 1.0, True)
-    np.testing.assert_allclose(dq[0, 0, 0], [math.log(3) / 3 - math.log(2) / 9, 0.0], atol=1e-15)
-    np.testing.assert_allclose(dk[0, :, 0], [[-2 / 9, 0], [-1 / 9, 0], [1 / 3, 0]], atol=1e-15)
-    np.testing.assert_allclose(dv[0, :, 0], [[1 / 6, 0], [1 / 3, 0], [1 / 2, 0]], atol=1e-15)
+    assert abs(delta[0, 0, 0] - _expr(bw["delta"])) < 1e-15
+    dq, dk, dv = oracle.attention_bwd_full(qa, k, v, do, lse, delta, q_idx, k_idx, scale, causal)
+    np.testing.assert_allclose(dq[0, 0, 0], _arr(bw["dQ"]), atol=1e-15)
+    np.testing.assert_allclose(dk[0, :, 0], _arr(bw["dK"]), atol=1e-15)
+    np.testing.assert_allclose(dv[0, :, 0], _arr(bw["dV"]), atol=1e-15)
 
 
 def _partials(rng, B=1, Sq=6, Hq=4, d=5, CP=4, masked=()):
