@@ -51,6 +51,31 @@ __device__ __forceinline__ void seg_tile_range(const int32_t* row, int n, int ti
   out_end = last + 1;
 }
 
+// Token span [lo, hi) of segment `s` in a row of `n` nondecreasing segment ids:
+// lo = first index with id >= s, hi = first index with id > s (binary searches).
+// With ids that decrease somewhere the span is some range inside [0, n] (never an
+// access outside the row).
+__device__ __forceinline__ void seg_span(const int32_t* row, int64_t n, int s, int64_t& lo, int64_t& hi) {
+  int64_t a = 0, b = n;
+  while (a < b) {
+    const int64_t m = (a + b) >> 1;
+    if (row[m] < s)
+      a = m + 1;
+    else
+      b = m;
+  }
+  lo = a;
+  b = n;
+  while (a < b) {
+    const int64_t m = (a + b) >> 1;
+    if (row[m] <= s)
+      a = m + 1;
+    else
+      b = m;
+  }
+  hi = a;
+}
+
 constexpr int kD128 = 128;
 constexpr int kD128Tile = 32;  // keys per staged tile of the dQ kernel
 
@@ -58,6 +83,9 @@ constexpr int kD128Tile = 32;  // keys per staged tile of the dQ kernel
 // (bwd_dq_d128.hip) on `stream`.
 ra_status launch_bwd_d128(BwdArgs args, hipStream_t stream);
 ra_status launch_dkdv_d128(BwdArgs args, hipStream_t stream);
+// dK/dV with 64 keys per wave (bwd_dkdv64_d128.hip) and its grid size.
+ra_status launch_dkdv64_d128(BwdArgs args, hipStream_t stream);
+int64_t dkdv64_d128_workgroups(const BwdArgs& args);
 ra_status launch_dq_d128(BwdArgs args, hipStream_t stream);
 
 }  // namespace ra

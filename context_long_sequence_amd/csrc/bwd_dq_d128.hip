@@ -277,7 +277,10 @@ ra_status launch_dq_d128(BwdArgs args, hipStream_t stream) {
 }
 
 ra_status launch_bwd_d128(BwdArgs args, hipStream_t stream) {
-  const ra_status st = launch_dkdv_d128(args, stream);
+  // dK/dV: 64 keys per wave (half the LDS operand bytes per MFMA) when that grid
+  // still gives each of the 256 CUs a workgroup; 32 keys per wave on small chunks.
+  const ra_status st = dkdv64_d128_workgroups(args) >= 256 ? launch_dkdv64_d128(args, stream)
+                                                            : launch_dkdv_d128(args, stream);
   if (st != RA_OK) return st;
   return launch_dq_d128(args, stream);
 }

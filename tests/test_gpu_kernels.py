@@ -147,6 +147,18 @@ STEP_CASES = [
 ]
 
 
+# Backward steps whose dK/dV grid (B * Hkv * ceil(Sk / 256) workgroups of 256 keys)
+# reaches 256, the size at which the bf16 d=128 backward runs 64 keys per wave.
+WIDE_BWD_CASES = [
+    ("bf16", 1, 333, 800, 128, 64, 128, 900, 300, True, False),   # diagonal, ragged on both sides
+    ("bf16", 2, 200, 1000, 64, 32, 128, 1000, 0, True, False),    # earlier chunk, ragged key tail
+    ("bf16", 1, 150, 777, 256, 64, 128, 0, 0, False, False),      # non-causal, GQA 4:1
+    ("bf16", 1, 512, 1024, 128, 64, 128, 512, 0, True, True),     # packed, diagonal chunk
+    ("bf16", 1, 300, 1000, 64, 64, 128, 0, 1000, False, True),    # packed, non-causal
+    ("bf16", 1, 100, 1024, 128, 64, 128, 0, 2048, True, False),   # chunk in the future: no live pair
+]
+
+
 def _step_case(case, seed):
     dtype, B, Sq, Sk, Hq, Hkv, d, q_off, kv_off, causal, packed = case
     rng = np.random.default_rng(seed)
@@ -184,7 +196,7 @@ def test_fwd_step_partial(case):
     assert np.all(on[np.transpose(dead, (0, 2, 1))] == 0)
 
 
-@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case", STEP_CASES + WIDE_BWD_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_bwd_step(case):
     """One backward step with the oracle's own final LSE/delta as inputs: dQ, dK, dV."""
     ra = lib()
