@@ -86,6 +86,9 @@ ra_status launch_dkdv_d128(BwdArgs args, hipStream_t stream);
 // dK/dV with 64 keys per wave (bwd_dkdv64_d128.hip) and its grid size.
 ra_status launch_dkdv64_d128(BwdArgs args, hipStream_t stream);
 int64_t dkdv64_d128_workgroups(const BwdArgs& args);
+// dQ with 64 queries per wave (bwd_dq64_d128.hip) and its grid size.
+ra_status launch_dq64_d128(BwdArgs args, hipStream_t stream);
+int64_t dq64_d128_workgroups(const BwdArgs& args);
 ra_status launch_dq_d128(BwdArgs args, hipStream_t stream);
 
 }  // namespace ra

@@ -282,7 +282,8 @@ ra_status launch_bwd_d128(BwdArgs args, hipStream_t stream) {
   const ra_status st = dkdv64_d128_workgroups(args) >= 256 ? launch_dkdv64_d128(args, stream)
                                                             : launch_dkdv_d128(args, stream);
   if (st != RA_OK) return st;
-  return launch_dq_d128(args, stream);
+  // dQ: 64 queries per wave on the same condition.
+  return dq64_d128_workgroups(args) >= 256 ? launch_dq64_d128(args, stream) : launch_dq_d128(args, stream);
 }
 
 }  // namespace ra

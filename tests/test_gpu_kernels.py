@@ -156,6 +156,14 @@ WIDE_BWD_CASES = [
     ("bf16", 1, 512, 1024, 128, 64, 128, 512, 0, True, True),     # packed, diagonal chunk
     ("bf16", 1, 300, 1000, 64, 64, 128, 0, 1000, False, True),    # packed, non-causal
     ("bf16", 1, 100, 1024, 128, 64, 128, 0, 2048, True, False),   # chunk in the future: no live pair
+    # dQ grid (B * Hkv * (group / h) * ceil(Sq / (256 / h)) workgroups, h = query heads per
+    # workgroup: 4, 2 or 1 by the GQA group) also at 256 or more: 64 queries per wave
+    ("bf16", 2, 500, 2000, 64, 16, 128, 1900, 300, True, False),  # group 4, diagonal, ragged
+    ("bf16", 1, 1000, 1024, 128, 64, 128, 1024, 0, True, False),  # group 2, earlier chunk
+    ("bf16", 1, 1000, 1100, 64, 64, 128, 0, 0, False, False),     # group 1, non-causal
+    ("bf16", 2, 512, 2048, 64, 16, 128, 1536, 0, True, True),     # group 4, packed, diagonal
+    ("bf16", 1, 1000, 1024, 64, 64, 128, 0, 1024, False, True),   # group 1, packed, non-causal
+    ("bf16", 2, 500, 2000, 64, 16, 128, 0, 3000, True, False),    # chunk in the future
 ]
 
 

@@ -52,10 +52,11 @@ def test_workspace_is_linear_in_the_chunk():
     assert 1.8 <= p2 / p1 <= 2.2
 
 
-@pytest.mark.parametrize("Sq,Sk,Hq,Hkv", [(320, 448, 8, 2), (320, 1000, 128, 64)])
+@pytest.mark.parametrize("Sq,Sk,Hq,Hkv", [(320, 448, 8, 2), (320, 1000, 128, 64), (1000, 1024, 128, 64)])
 def test_bwd_step_is_bitwise_repeatable(Sq, Sk, Hq, Hkv):
-    """Both dK/dV kernels (32 keys per wave; 64 keys per wave on the second, wide
-    grid) and the dQ kernel give the same bits on every call."""
+    """Both dK/dV kernels (32 keys per wave; 64 keys per wave on the wider grids) and
+    both dQ kernels (32 queries per wave; 64 on the last grid) give the same bits on
+    every call."""
     ra = lib()
     rng = np.random.default_rng(3)
     B, d = 1, 128
