@@ -377,6 +377,19 @@ def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_wor
     def bf(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
 
+    def grad_buffers(q, ks):
+        """fp32 dQ and per-chunk dK/dV accumulators, allocated once."""
+        return {"dq": torch.empty(q.shape, dtype=torch.float32, device=dev),
+                "dk_chunks": [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in ks],
+                "dv_chunks": [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in ks]}
+
+    def zeroed(gb):
+        """Clears the accumulators (part of each timed backward, as in the main step)."""
+        gb["dq"].zero_()
+        for x in gb["dk_chunks"] + gb["dv_chunks"]:
+            x.zero_()
+        return gb
+
     # 8K Llama-3-8B-shaped share (rank 3 of 4), forward
     c2 = LLAMA3_8K_FWD
     wl = make_workload(c2, q_chunks=[c2.rank])
@@ -385,6 +398,18 @@ def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_wor
     ms = ev_ms(lambda: ra.ring_forward(q, ks, vs, c2.rank, c2.CP, causal=True, workspace=ws))
     pairs = live_pairs_causal(c2.C, c2.rank)
     out["fwd_8k_cp4_r3"] = {"ms": round(ms, 4), "tflops": round(4.0 * c2.Hq * c2.d * pairs / (ms * 1e-3) / 1e12, 2)}
+    # the same share's backward (dO ~ N(0,1)), from the forward's O and LSE
+    o2 = torch.empty_like(q)
+    l2 = torch.empty((1, c2.Hq, c2.C), dtype=torch.float32, device=dev)
+    ws = ra.RingWorkspace(1, c2.C, c2.Hq, c2.d, dev, backward=True)
+    ra.ring_forward(q, ks, vs, c2.rank, c2.CP, causal=True, workspace=ws, out=o2, lse=l2)
+    do2 = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(5), device=dev).to(torch.bfloat16)
+    g2 = grad_buffers(q, ks)
+    bms = ev_ms(lambda: ra.ring_backward(q, ks, vs, o2, l2, do2, c2.rank, c2.CP, causal=True, delta=ws.delta,
+                                         **zeroed(g2)))
+    out["bwd_8k_cp4_r3"] = {"ms": round(bms, 4),
+                            "tflops": round(10.0 * c2.Hq * c2.d * pairs / (bms * 1e-3) / 1e12, 2)}
+    del o2, l2, do2
 
     # packed 16K share (rank 2 of 4): segment ids + forward + backward
     c4 = PACKED16K_FWD.with_(backward=True)
@@ -399,8 +424,9 @@ def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_wor
     l4 = torch.empty((1, c4.Hq, c4.C), dtype=torch.float32, device=dev)
     fms = ev_ms(lambda: ra.ring_forward(q, ks, vs, c4.rank, c4.CP, causal=True, seg_ids=seg, workspace=ws,
                                          out=o4, lse=l4))
+    g4 = grad_buffers(q, ks)
     bms = ev_ms(lambda: ra.ring_backward(q, ks, vs, o4, l4, do, c4.rank, c4.CP, causal=True, seg_ids=seg,
-                                         delta=ws.delta))
+                                         delta=ws.delta, **zeroed(g4)))
     pairs4 = packed_live_pairs(wl.lengths, c4.C, c4.rank)
     out["packed_16k_cp4_r2"] = {
         "live_pairs": pairs4, "frac_of_causal_pairs": round(pairs4 / live_pairs_causal(c4.C, c4.rank), 4),

@@ -7,6 +7,8 @@
 // operands of dQ^T += K^T dS^T come from transposing reads of the same K tile.
 #include "bwd_d128.h"
 
+#include <mutex>
+
 namespace ra {
 namespace {
 
@@ -276,14 +278,55 @@ ra_status launch_dq_d128(BwdArgs args, hipStream_t stream) {
   return check_launch("ring_attn_bwd_step (dQ)");
 }
 
+// One side stream per device (default priority, non-blocking) with a fork and a
+// join event.  The dQ kernel of a step runs there while the dK/dV kernel of the
+// same step runs on the caller's stream: the two read the same inputs and write
+// disjoint outputs, and when one of them leaves CUs idle (a small grid, the
+// uneven causal diagonal) the other fills them.  dK/dV, the longer of the two, is
+// queued first so that its workgroups are placed first.  The caller's stream
+// waits on the join, so the step is complete in that stream's order like a single
+// launch.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mutex;
+
+ra_status side_stream_locked(SideStream*& out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(RA_ERR_HIP, "ring_attn_bwd_step: no current device");
+  SideStream& ss = g_side[dev];
+  if (!ss.stream) {
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return fail(RA_ERR_HIP, "ring_attn_bwd_step: side stream creation failed");
+  }
+  out = &ss;
+  return RA_OK;
+}
+
 ra_status launch_bwd_d128(BwdArgs args, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_side_mutex);
+  SideStream* ss = nullptr;
+  ra_status st = side_stream_locked(ss);
+  if (st != RA_OK) return st;
+  if (hipEventRecord(ss->fork, stream) != hipSuccess || hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess)
+    return fail(RA_ERR_HIP, "ring_attn_bwd_step: fork to the side stream failed");
   // dK/dV: 64 keys per wave (half the LDS operand bytes per MFMA) when that grid
   // still gives each of the 256 CUs a workgroup; 32 keys per wave on small chunks.
-  const ra_status st = dkdv64_d128_workgroups(args) >= 256 ? launch_dkdv64_d128(args, stream)
-                                                            : launch_dkdv_d128(args, stream);
+  st = dkdv64_d128_workgroups(args) >= 256 ? launch_dkdv64_d128(args, stream) : launch_dkdv_d128(args, stream);
   if (st != RA_OK) return st;
   // dQ: 64 queries per wave on the same condition.
-  return dq64_d128_workgroups(args) >= 256 ? launch_dq64_d128(args, stream) : launch_dq_d128(args, stream);
+  st = dq64_d128_workgroups(args) >= 256 ? launch_dq64_d128(args, ss->stream) : launch_dq_d128(args, ss->stream);
+  if (st != RA_OK) return st;
+  if (hipEventRecord(ss->join, ss->stream) != hipSuccess || hipStreamWaitEvent(stream, ss->join, 0) != hipSuccess)
+    return fail(RA_ERR_HIP, "ring_attn_bwd_step: join from the side stream failed");
+  return RA_OK;
 }
 
 }  // namespace ra
