@@ -79,14 +79,22 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     qt_begin = (int)min<int64_t>((int64_t)n_qt, max<int64_t>(0, first_q) / QT);
   }
   int seg_k = 0;
-  int seg_w_lo = 0, seg_w_hi = 0;  // segment ids of the wave's first and last key
   const int32_t* seg_row = nullptr;
+  // Packed rows: when every key of the workgroup is in one segment, the query tiles
+  // that lie entirely inside that segment, [full_lo, full_hi), need no segment test.
+  bool one_seg = !kSeg;
+  int64_t full_lo = 0, full_hi = n_qt;
   if constexpr (kSeg) {
     seg_row = a.seg + (int64_t)b * a.seg_len;
     seg_k = k_valid ? seg_row[kgl] : INT32_MIN;
-    seg_w_lo = seg_row[a.kv_offset + min(kw, a.Sk - 1)];
-    seg_w_hi = seg_row[a.kv_offset + min(kw + 32, a.Sk) - 1];
     const int lo = seg_row[a.kv_offset + k0], hi = seg_row[a.kv_offset + k_last];
+    if (lo == hi) {
+      int64_t sp_lo, sp_hi;  // the segment's token span in the row
+      seg_span(seg_row, a.seg_len, lo, sp_lo, sp_hi);
+      full_lo = max<int64_t>(0, sp_lo - a.q_offset + QT - 1) / QT;
+      full_hi = min<int64_t>(n_qt, max<int64_t>(0, sp_hi - a.q_offset) / QT);
+      one_seg = true;
+    }
     int sb, se;
     seg_tile_range(seg_row + a.q_offset, a.Sq, QT, qt_begin, qt_end, lo, hi, sb, se);
     qt_begin = sb;
@@ -99,18 +107,22 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   // workgroup may be invisible (they run the masked body), then the rest (the
   // unmasked body, no selects).  Per query head the masked tiles are a prefix
   // [qt_begin, qt_begin + n_pre) (the causal diagonal: tiles whose first query
-  // precedes the workgroup's last key) and, when the shard ends inside a tile, the
-  // last tile.  A workgroup with keys past the chunk end, and every packed-row
-  // workgroup, runs all its tiles masked.
+  // precedes the workgroup's last key; for packed rows also the tiles before the
+  // first one inside the keys' segment) and one last tile when the shard ends inside
+  // it (or, packed, when it reaches past the segment's end).  A workgroup with keys
+  // past the chunk end, or with keys of two segments, runs all its tiles masked.
   int n_pre = n_q, n_tail = 0;
-  if (!kSeg && k0 + 32 * NW <= a.Sk) {
+  if (one_seg && k0 + 32 * NW <= a.Sk) {
     int64_t diag_end = qt_begin;  // first tile whose first query follows the workgroup's last key
     if (a.causal) {
       const int64_t last_rel = a.kv_offset + k0 + 32 * NW - 1 - a.q_offset;  // last key, in query coordinates
       diag_end = last_rel < 0 ? 0 : last_rel / QT + 1;
     }
+    if constexpr (kSeg) diag_end = max<int64_t>(diag_end, full_lo);
     n_pre = (int)min<int64_t>(n_q, max<int64_t>(0, diag_end - qt_begin));
-    n_tail = (a.Sq % QT != 0 && qt_end - 1 >= qt_begin + n_pre) ? 1 : 0;
+    bool tail = a.Sq % QT != 0;
+    if constexpr (kSeg) tail |= qt_end > full_hi;
+    n_tail = (tail && qt_end - 1 >= qt_begin + n_pre) ? 1 : 0;
   }
   const int n_m = n_pre + n_tail;     // masked tiles per query head
   const int n_u = n_q - n_m;          // unmasked tiles per query head

@@ -34,21 +34,6 @@ constexpr int kNW = 4;   // waves per workgroup
 constexpr int kQW = 64;  // queries per wave
 constexpr int kKT = 32;  // keys per staged tile
 
-// D = A*B + C with B in AGPRs, C and D in VGPRs (D early-clobber: it must not share
-// registers with A, B or C).
-__device__ __forceinline__ void mfma_vab(f32x16& d, bf16x8 a, bf16x8 b, const f32x16& c) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
-}
-__device__ __forceinline__ void mfma_vab0(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_vab_acc(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-// Wait states between an MFMA that wrote a VGPR and the first vector instruction
-// that reads it (more than the 8-pass MFMA's requirement).
-__device__ __forceinline__ void mfma_read_gap() { asm volatile("s_nop 7\n\ts_nop 7"); }
-
 // Heads per workgroup: the largest of 4, 2, 1 that divides the GQA group.
 __host__ __device__ __forceinline__ int dq64_heads_per_wg(int group) {
   return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);

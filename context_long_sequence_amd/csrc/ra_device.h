@@ -52,6 +52,24 @@ __device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// D = A*B + C with B in AGPRs, C and D in VGPRs (D early-clobber: it must not share
+// registers with A, B or C).
+__device__ __forceinline__ void mfma_vab(f32x16& d, bf16x8 a, bf16x8 b, const f32x16& c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+}
+__device__ __forceinline__ void mfma_vab0(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_vab_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// Wait states between an MFMA that wrote a VGPR and the first vector instruction
+// that reads it (more than the 8-pass MFMA's requirement).
+__device__ __forceinline__ void mfma_read_gap() { asm volatile("s_nop 7\n\ts_nop 7"); }
+// Wait states between the last of a run of MFMAs that accumulate in AGPRs and any
+// other instruction that reads those AGPRs (the 16-pass requirement, with margin).
+__device__ __forceinline__ void mfma_acc_gap() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"); }
+
 // Negation of 8 bf16 values (sign bits flipped: exact).
 __device__ __forceinline__ bf16x8 neg_bf16x8(bf16x8 v) {
   const u32x4 m = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
@@ -248,6 +266,56 @@ __device__ __forceinline__ int xcd_logical_id(int w, int n) {
   const int base = n / kXcd, rem = n % kXcd;
   // XCD x owns base + (x < rem) ids; its range starts at x*base + min(x, rem).
   return xcd * base + min(xcd, rem) + local;
+}
+
+// Contiguous range [begin, end) of tiles (of `tile` items over `n` items of the
+// row starting at `row`) whose segment-id range meets [lo, hi].  Segment ids are
+// nondecreasing along the row, so the live tiles are contiguous.  Wave-uniform.
+__device__ __forceinline__ void seg_tile_range(const int32_t* row, int n, int tile, int t_begin, int t_end,
+                                               int lo, int hi, int& out_begin, int& out_end) {
+  const int lane = threadIdx.x & 63;
+  int first = t_end, last = -1;
+  for (int base = t_begin; base < t_end; base += 64) {
+    const int t = base + lane;
+    bool live = false;
+    if (t < t_end) {
+      const int a = t * tile;
+      const int z = min((t + 1) * tile, n) - 1;
+      live = row[z] >= lo && row[a] <= hi;
+    }
+    const uint64_t mask = __ballot(live);
+    if (mask) {
+      first = min(first, base + (int)__builtin_ctzll(mask));
+      last = max(last, base + 63 - (int)__builtin_clzll(mask));
+    }
+  }
+  out_begin = first;
+  out_end = last + 1;
+}
+
+// Token span [lo, hi) of segment `s` in a row of `n` nondecreasing segment ids:
+// lo = first index with id >= s, hi = first index with id > s (binary searches).
+// With ids that decrease somewhere the span is some range inside [0, n] (never an
+// access outside the row).
+__device__ __forceinline__ void seg_span(const int32_t* row, int64_t n, int s, int64_t& lo, int64_t& hi) {
+  int64_t a = 0, b = n;
+  while (a < b) {
+    const int64_t m = (a + b) >> 1;
+    if (row[m] < s)
+      a = m + 1;
+    else
+      b = m;
+  }
+  lo = a;
+  b = n;
+  while (a < b) {
+    const int64_t m = (a + b) >> 1;
+    if (row[m] <= s)
+      a = m + 1;
+    else
+      b = m;
+  }
+  hi = a;
 }
 
 }  // namespace ra

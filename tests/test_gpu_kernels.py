@@ -166,17 +166,39 @@ WIDE_BWD_CASES = [
     ("bf16", 2, 500, 2000, 64, 16, 128, 0, 3000, True, False),    # chunk in the future
 ]
 
+# Forward steps on grids of 512 or more workgroups of 64-query waves (B * Hkv * (group
+# / h) * ceil(Sq / (256 / h)), h = 4, 2 or 1 query heads per workgroup by the GQA
+# group): the size at which the bf16 d=128 forward of packed rows runs 64 queries per
+# wave, and wide grids of the 8-wave kernel otherwise.
+WIDE_FWD_CASES = [
+    ("bf16", 2, 4100, 600, 16, 4, 128, 500, 300, True, False),     # group 4, diagonal, ragged
+    ("bf16", 1, 8200, 500, 16, 8, 128, 0, 0, False, False),        # group 2, non-causal
+    ("bf16", 2, 4100, 700, 16, 16, 128, 4000, 3900, True, False),  # group 1, diagonal
+    ("bf16", 2, 4100, 1000, 16, 4, 128, 1000, 0, True, True),      # group 4, packed, earlier chunk
+    ("bf16", 1, 4096, 512, 32, 8, 128, 0, 5000, True, False),      # chunk in the future
+]
+
+
+# Packed rows with long samples (lengths drawn from the given range): whole query
+# tiles and key blocks inside one sample, which run without the segment test.
+LONG_SEG_CASES = [
+    ("bf16", 1, 1024, 2048, 32, 8, 128, 2048, 0, True, (300, 1200)),    # earlier chunk
+    ("bf16", 1, 1024, 1024, 32, 8, 128, 1024, 1024, True, (300, 1200)),  # diagonal chunk
+    ("bf16", 2, 1000, 1100, 16, 4, 128, 1100, 0, True, (150, 900)),     # ragged tails
+]
+
 
 def _step_case(case, seed):
     dtype, B, Sq, Sk, Hq, Hkv, d, q_off, kv_off, causal, packed = case
     rng = np.random.default_rng(seed)
     q, k, v = _qkv(rng, B, Sq, Sk, Hq, Hkv, d, dtype)
     S = max(q_off + Sq, kv_off + Sk)
-    seg = oracle.segment_ids(_packed_pos(rng, B, S, 20, 200)) if packed else None
+    lo, hi = (20, 200) if packed is True else (packed or (0, 0))
+    seg = oracle.segment_ids(_packed_pos(rng, B, S, lo, hi)) if packed else None
     return q, k, v, seg, S
 
 
-@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case", STEP_CASES + WIDE_FWD_CASES + LONG_SEG_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_fwd_step_partial(case):
     ra = lib()
     dtype, B, Sq, Sk, Hq, Hkv, d, q_off, kv_off, causal, packed = case
@@ -204,7 +226,7 @@ def test_fwd_step_partial(case):
     assert np.all(on[np.transpose(dead, (0, 2, 1))] == 0)
 
 
-@pytest.mark.parametrize("case", STEP_CASES + WIDE_BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case", STEP_CASES + WIDE_BWD_CASES + LONG_SEG_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_bwd_step(case):
     """One backward step with the oracle's own final LSE/delta as inputs: dQ, dK, dV."""
     ra = lib()
@@ -294,7 +316,8 @@ def test_step_with_peaked_scores(gain, causal, Sq, Sk, q_off, kv_off):
 
 
 @pytest.mark.parametrize("out", [None, "same", "f32"])
-@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case", STEP_CASES + WIDE_FWD_CASES[:1] + WIDE_FWD_CASES[3:4],
+                         ids=lambda c: "-".join(map(str, c)))
 def test_fwd_step_merge_equals_step_then_merge(case, out):
     """ring_attn_fwd_step_merge gives the same bits as ring_attn_fwd_step followed by
     lse_merge: running result with live rows, rows that have seen no key yet
@@ -330,8 +353,8 @@ def test_fwd_step_merge_equals_step_then_merge(case, out):
 
 
 WIDE_CASES = [
-    # (Sq, Sk, q_off, kv_off, causal): 128 query heads x ceil(Sq / 256) >= 1024 query tiles
-    # of 256 rows, the grid size at which the bf16 d=128 forward uses 8-wave workgroups.
+    # (Sq, Sk, q_off, kv_off, causal): 128 query heads (GQA 16:1) over 8 KV heads, a grid
+    # of 64-query waves with four query heads per workgroup.
     (1900, 2100, 2100, 2100, True),   # diagonal chunk, ragged tails on both sides
     (1900, 2100, 2100, 0, True),      # earlier chunk: every block fully visible
     (2048, 1500, 900, 1200, True),    # partly in the future: some rows see nothing
@@ -341,9 +364,9 @@ WIDE_CASES = [
 
 @pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_fwd_step_wide_grid(case):
-    """A forward step on a grid large enough for the 8-wave workgroup variant: full
-    comparison with the oracle on a subset of query heads (each head is an
-    independent attention problem over its own KV head)."""
+    """A forward step on a wide grid (GQA 16:1): comparison with the oracle on a
+    subset of query heads (each head is an independent attention problem over its
+    own KV head)."""
     ra = lib()
     Sq, Sk, q_off, kv_off, causal = case
     B, Hq, Hkv, d = 1, 128, 8, 128
