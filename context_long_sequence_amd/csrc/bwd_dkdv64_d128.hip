@@ -427,6 +427,10 @@ __global__ __launch_bounds__(64 * kNW) void dkdv64_d128_kernel(BwdArgs a) {
       }
       fence();
     }
+    // Wait states behind the last accumulating MFMA before any branch: on the
+    // loop's exit path the compiler may copy the accumulators at once.
+    mfma_acc_gap();
+    fence();
   };
 
   // Prologue: copies of tiles 0 and 1, wave 0 rescales tile 0's LSE row, the barrier

@@ -403,6 +403,10 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
       if (k < 8 && k % 2 == 0) read_tr(1, 1, db);
       fence();
     }
+    // Wait states behind the last accumulating MFMA before any branch: on the
+    // loop's exit path the compiler may copy the accumulators at once.
+    mfma_acc_gap();
+    fence();
   };
 
   // One step: wait for tile `it` (copies issued two steps ago), publish it to the

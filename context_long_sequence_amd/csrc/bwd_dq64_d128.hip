@@ -323,7 +323,6 @@ __global__ __launch_bounds__(64 * kNW) void dq64_d128_kernel(BwdArgs a) {
     constexpr int pc = decltype(par_tag)::value, pn = pc ^ 1;  // buffers of tiles t and t+1
     const int k0n = (kt_begin + t + 1) * kKT;  // tile t+1's first key
     opaque_bases();
-    mfma_read_gap();
     fence();
     // ---- phase 1: S^T of tile t+1 | dS of tile t and its packing; tile t's first
     // K^T operands
@@ -368,6 +367,11 @@ __global__ __launch_bounds__(64 * kNW) void dq64_d128_kernel(BwdArgs a) {
       preload(k, false, k2, okn);
       if (k == 15) stage_c(pn, 1, 15);
     });
+    // Wait states behind the last dP^T MFMA before any branch: past a loop exit its
+    // registers are free, and an instruction that reused one could be overwritten by
+    // the MFMA's late write.
+    mfma_read_gap();
+    fence();
   };
 
   // Prologue: copies of tiles 0..3, the barrier that publishes tiles 0 and 1, then
