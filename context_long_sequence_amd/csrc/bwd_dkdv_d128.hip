@@ -102,6 +102,8 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   }
   const int n_q = qt_end - qt_begin;
   const int n_iter = n_q * group;
+  // A workgroup without a live tile adds exactly zero to every accumulator: done.
+  if (n_iter <= 0) return;
 
   // Tile order: first the tiles in which some element of some wave of the
   // workgroup may be invisible (they run the masked body), then the rest (the

@@ -94,6 +94,8 @@ __global__ __launch_bounds__(64 * kNW) void dq64_d128_kernel(BwdArgs a) {
     kt_end = max(sb, se);
   }
   const int n_t = kt_end - kt_begin;
+  // A workgroup without a live tile adds exactly zero to every accumulator: done.
+  if (n_t <= 0) return;
 
   // Per lane and query block qb: the query q = qw + 32 qb + col, its Q and dO rows
   // (B operands; lane = query column, k-slots = d), -LSE*log2(e), and -delta

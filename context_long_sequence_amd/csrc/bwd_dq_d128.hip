@@ -80,6 +80,8 @@ __global__ __launch_bounds__(kDqThreads) void dq_d128_kernel(BwdArgs a) {
     kt_begin = sb;
     kt_end = max(sb, se);
   }
+  // A workgroup without a live tile adds exactly zero to every accumulator: done.
+  if (kt_begin >= kt_end) return;
 
   bf16x8 qf[8], dof[8];
   {

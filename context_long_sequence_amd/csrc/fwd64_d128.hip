@@ -99,6 +99,9 @@ __global__ __launch_bounds__(64 * kNW) void fwd64_d128_kernel(FwdArgs a) {
     kt_end = max(sb, se);
   }
   const int n_t = kt_end - kt_begin;
+  // Merging a step without a live tile into the running result changes nothing:
+  // unless the merged output is also converted, the workgroup is done.
+  if (n_t <= 0 && a.merge && a.out_kind == 0) return;
 
   // Per lane and query block qb: the query q = qw + 32 qb + col, its Q row (B
   // operands; lane = query column, k-slots = d), and the chunk keys it sees,

@@ -415,6 +415,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
     kt_begin = first_live;
     kt_end = max(first_live, last_live + 1);
   }
+  // Merging a step without a live tile into the running result changes nothing:
+  // unless the merged output is also converted, the workgroup is done.
+  if (kt_begin >= kt_end && a.merge && a.out_kind == 0) return;
 
   // Q operands (B of S^T = K Q^T).
   bf16x8 qf[8];
