@@ -96,8 +96,6 @@ __global__ __launch_bounds__(64 * kNW) void dkdv64_d128_kernel(BwdArgs a) {
   }
   const int n_q = qt_end - qt_begin;
   const int n_iter = n_q * group;
-  // A workgroup without a live tile adds exactly zero to every accumulator: done.
-  if (n_iter <= 0) return;
 
   // Tile order: first the tiles in which some element of some wave may be
   // invisible (they run the masked body), then the rest (the unmasked body).  Per
@@ -477,6 +475,10 @@ __global__ __launch_bounds__(64 * kNW) void dkdv64_d128_kernel(BwdArgs a) {
     if (it + 3 < n_iter) tile(um, it + 3, qs3, ds3, xs3, qs0, xs0, qs2, ds2, xs2, fq0, fq1, lsv);
   }
 
+  // A workgroup without a live tile adds exactly zero to every accumulator: done.
+  // (Tested here rather than before the loop: an early exit there costs the loop
+  // registers.)
+  if (n_iter <= 0) return;
   // The accumulators were last written by inline-asm MFMAs, which the compiler's
   // hazard tracking does not see: wait out the MFMA write latency before they are read.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"

@@ -8,6 +8,8 @@
 // registers) two steps ahead into a ring of three slots; their transposes are
 // read with transposing LDS reads.  The tile body is a hand-placed MFMA / vector
 // ALU pipeline (see compute below).
+#include <algorithm>
+
 #include "bwd_d128.h"
 
 
@@ -15,6 +17,7 @@ namespace ra {
 namespace {
 
 constexpr int kD = kD128;
+constexpr int kMinSplitTiles = 8;  // fewest tile positions per workgroup of a split key block
 
 // ------------------------------------------------------------------------------------
 // dK, dV: NW waves x 32 keys of one KV head; walks the 32-query tiles of every
@@ -37,13 +40,18 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) float xs0[4 * QT];
   __shared__ __attribute__((aligned(1024))) float xs1[4 * QT];
   __shared__ __attribute__((aligned(1024))) float xs2[4 * QT];
+  __shared__ int last_flag;  // split key blocks: this workgroup completes the block
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int kt = logical % a.n_tiles;
-  const int g = (logical / a.n_tiles) % a.Hkv;
-  const int b = logical / a.n_tiles / a.Hkv;
+  // Workgroup -> (b, kv head, key block, split); the splits of a key block are
+  // consecutive, so they run on one XCD.
+  const int split = logical % a.n_split;
+  const int kblk = logical / a.n_split;  // key block, linear over (b, kv head, key tile)
+  const int kt = kblk % a.n_tiles;
+  const int g = (kblk / a.n_tiles) % a.Hkv;
+  const int b = kblk / a.n_tiles / a.Hkv;
   const int group = a.Hq / a.Hkv;
 
   const int k0 = kt * 32 * NW;
@@ -104,6 +112,13 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   const int n_iter = n_q * group;
   // A workgroup without a live tile adds exactly zero to every accumulator: done.
   if (n_iter <= 0) return;
+  // Split of the key block's n_iter tile positions (walk order below) over n_sp
+  // workgroups, at least kMinSplitTiles positions each; workgroups past n_sp have
+  // nothing to do.  This workgroup takes positions [p_begin, p_begin + len).
+  const int n_sp = max(1, min(a.n_split, n_iter / kMinSplitTiles));
+  if (split >= n_sp) return;
+  const int p_begin = (int)((int64_t)n_iter * split / n_sp);
+  const int len = (int)((int64_t)n_iter * (split + 1) / n_sp) - p_begin;
 
   // Tile order: first the tiles in which some element of some wave of the
   // workgroup may be invisible (they run the masked body), then the rest (the
@@ -149,7 +164,12 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
       }
     }
   };
-  TileWalk issue_walk{0, 0, n_m > 0}, compute_walk{0, 0, n_m > 0};
+  auto walk_at = [&](int pos) {  // the walker at position pos of the order
+    if (pos < n_masked) return TileWalk{pos / n_m, pos % n_m, true};
+    const int u = pos - n_masked;
+    return TileWalk{u / n_u, u % n_u, false};
+  };
+  TileWalk issue_walk = walk_at(p_begin), compute_walk = walk_at(p_begin);
 
   // Visibility of query q0 + 16*half + i to this lane's key: lo - q0 <= i < hi - q0
   // (causal rule and the end of the query shard; 32-bit: offsets clamped to +-2^30,
@@ -420,18 +440,18 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   auto step = [&](auto mask_tag, int it, const __bf16* qc, const __bf16* dc, const float* xc, float* x1,
                   __bf16* qn, __bf16* dn, float* xn) {
     asm volatile("" ::: "memory");
-    if (it + 1 < n_iter)
+    if (it + 1 < len)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCopiesPerTile));  // tile it+1 may stay in flight
     else
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (it + 2 < n_iter) issue(qn, dn, xn);
-    const bool resc = wave == 0 && it + 1 < n_iter;
+    if (it + 2 < len) issue(qn, dn, xn);
+    const bool resc = wave == 0 && it + 1 < len;
     float lraw = 0.0f;
     if (resc) {
-      rescale_wait(it + 2 < n_iter);
+      rescale_wait(it + 2 < len);
       lraw = x1[lane];
     }
     compute(mask_tag, it, qc, dc, xc);
@@ -441,26 +461,28 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     }
   };
 
-  if (n_iter > 0) issue(qs0, ds0, xs0);
-  if (n_iter > 1) issue(qs1, ds1, xs1);
-  if (wave == 0 && n_iter > 0) {
-    rescale_wait(n_iter > 1);
+  // Steps it = 0 .. len-1 visit positions p_begin + it.
+  issue(qs0, ds0, xs0);
+  if (len > 1) issue(qs1, ds1, xs1);
+  if (wave == 0) {
+    rescale_wait(len > 1);
     xs0[lane] = xs0[lane] * -kLog2e;
   }
   // Masked tiles first, in whole groups of three (a group that reaches into the
   // unmasked tiles runs masked: correct, only slower), so that both loops start at
   // slot 0 of the ring.
-  const int n_masked3 = min(n_iter, (n_masked + 2) / 3 * 3);
+  const int n_masked_here = max(0, min(len, n_masked - p_begin));
+  const int n_masked3 = min(len, (n_masked_here + 2) / 3 * 3);
   int it = 0;
   for (; it < n_masked3; it += 3) {
     step(BoolTag<true>{}, it, qs0, ds0, xs0, xs1, qs2, ds2, xs2);
-    if (it + 1 < n_iter) step(BoolTag<true>{}, it + 1, qs1, ds1, xs1, xs2, qs0, ds0, xs0);
-    if (it + 2 < n_iter) step(BoolTag<true>{}, it + 2, qs2, ds2, xs2, xs0, qs1, ds1, xs1);
+    if (it + 1 < len) step(BoolTag<true>{}, it + 1, qs1, ds1, xs1, xs2, qs0, ds0, xs0);
+    if (it + 2 < len) step(BoolTag<true>{}, it + 2, qs2, ds2, xs2, xs0, qs1, ds1, xs1);
   }
-  for (; it < n_iter; it += 3) {
+  for (; it < len; it += 3) {
     step(BoolTag<false>{}, it, qs0, ds0, xs0, xs1, qs2, ds2, xs2);
-    if (it + 1 < n_iter) step(BoolTag<false>{}, it + 1, qs1, ds1, xs1, xs2, qs0, ds0, xs0);
-    if (it + 2 < n_iter) step(BoolTag<false>{}, it + 2, qs2, ds2, xs2, xs0, qs1, ds1, xs1);
+    if (it + 1 < len) step(BoolTag<false>{}, it + 1, qs1, ds1, xs1, xs2, qs0, ds0, xs0);
+    if (it + 2 < len) step(BoolTag<false>{}, it + 2, qs2, ds2, xs2, xs0, qs1, ds1, xs1);
   }
 
   // The accumulators were last written by inline-asm MFMAs, which the compiler's
@@ -476,6 +498,55 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   const float ks = -a.scale;  // dk holds -sum dS^T q (the dP chain runs on negated V)
   const int64_t base = ((int64_t)b * a.Sk + kw) * kv_rs + (int64_t)g * kD + col;
   const bool full = kw + 32 <= a.Sk;
+  if (n_sp > 1) {
+    // Partial sums of a split key block: each workgroup stores its accumulators,
+    // then counts itself in; the one that arrives last reads all n_sp partials back
+    // and adds them up in split order (the result does not depend on arrival order)
+    // before the read-modify-write of dK and dV.  The partials are written through
+    // to, and read from, the memory side of the per-XCD L2 caches (the sc1 cache
+    // policy of agent-scope coherence), which needs no cache-wide fence; every store
+    // of this wave has completed (vmcnt 0) before the workgroup barrier and the
+    // count.  Layout per workgroup: [tensor][wave][db][lane][16 registers].
+    constexpr int kSc1 = 16;  // cache policy bits: sc1
+    const buffer_rsrc pr = make_rsrc32(reinterpret_cast<char*>(a.part) + (int64_t)kblk * a.n_split * kDkdvPartPerWg,
+                                       a.n_split * (int)kDkdvPartPerWg);
+    auto poff = [&](int sp, int tensor, int db, int j4) {
+      return (int)(((((sp * 2 + tensor) * NW + wave) * 4 + db) * 64 + lane) * 64 + 16 * j4);
+    };
+    auto put = [&](const f32x16& x, int tensor, int db) {
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const f32x4 v = {x[4 * j4], x[4 * j4 + 1], x[4 * j4 + 2], x[4 * j4 + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), pr, poff(split, tensor, db, j4), 0,
+                                               kSc1);
+      }
+    };
+    auto add_from = [&](f32x16& x, int sp, int tensor, int db, bool first) {
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, poff(sp, tensor, db, j4), 0, kSc1));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * j4 + e] = first ? v[e] : x[4 * j4 + e] + v[e];
+      }
+    };
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      put(dk[db], 0, db);
+      put(dv[db], 1, db);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (tid == 0)
+      last_flag = __hip_atomic_fetch_add(a.count + kblk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_sp - 1;
+    __syncthreads();
+    if (!last_flag) return;
+    for (int sp = 0; sp < n_sp; ++sp)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        add_from(dk[db], sp, 0, db, sp == 0);
+        add_from(dv[db], sp, 1, db, sp == 0);
+      }
+  }
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     float ok[16], ov[16];
@@ -502,11 +573,47 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
 
 }  // namespace
 
-ra_status launch_dkdv_d128(BwdArgs args, hipStream_t stream) {
+// Workgroups per key block.  Key blocks that see very different numbers of query
+// tiles -- the causal diagonal chunk, packed rows -- leave most CUs idle behind
+// their longest block; two workgroups per block halve that block's run.  Uniform
+// chunks keep one: their dQ kernel already runs beside them on the other CUs.
+int dkdv_d128_split(const BwdArgs& args) {
+  constexpr int NW = 4;
+  const int64_t n_blk = (int64_t)args.B * args.Hkv * ((args.Sk + 32 * NW - 1) / (32 * NW));
+  if (n_blk > kDkdvCounters) return 1;
+  const bool diagonal =
+      args.causal && args.kv_offset + args.Sk > args.q_offset && args.kv_offset < args.q_offset + args.Sq;
+  int s = (args.seg != nullptr || diagonal) ? 2 : 1;
+  while (s > 1 && (size_t)(s * n_blk) * kDkdvPartPerWg > kDkdvPartBytes) --s;
+  return s;
+}
+
+namespace {
+__global__ void zero_counts_kernel(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+}  // namespace
+
+ra_status launch_dkdv_d128(BwdArgs args, hipStream_t stream, void* scratch) {
   constexpr int NW = 4;  // waves (x 32 keys) per workgroup
   args.n_tiles = (args.Sk + 32 * NW - 1) / (32 * NW);
-  const int64_t n_wg = (int64_t)args.B * args.Hkv * args.n_tiles;
+  args.n_split = dkdv_d128_split(args);
+  const int64_t n_blk = (int64_t)args.B * args.Hkv * args.n_tiles;
+  const int64_t n_wg = n_blk * args.n_split;
   if (n_wg > INT32_MAX) return fail(RA_ERR_INVALID_ARGUMENT, "too many workgroups");
+  args.count = nullptr;
+  args.part = nullptr;
+  if (args.n_split > 1) {
+    if (!scratch) return fail(RA_ERR_INVALID_ARGUMENT, "ring_attn_bwd_step: split dK/dV needs scratch");
+    args.count = static_cast<int*>(scratch);
+    args.part = reinterpret_cast<float*>(static_cast<char*>(scratch) + kDkdvCountBytes);
+    // The arrival counters start at zero (a fill kernel: no memset node in a graph).
+    hipLaunchKernelGGL(zero_counts_kernel, dim3((unsigned)((n_blk + 255) / 256)), dim3(256), 0, stream, args.count,
+                       (int)n_blk);
+    const ra_status st = check_launch("ring_attn_bwd_step (dK/dV counters)");
+    if (st != RA_OK) return st;
+  }
   if (args.seg)
     hipLaunchKernelGGL((dkdv_d128_kernel<true, NW>), dim3((unsigned)n_wg), dim3(64 * NW), 0, stream, args);
   else

@@ -20,6 +20,7 @@
 //    and walks the key tiles like the forward (query in the lane); K is staged
 //    row-major and transposed, V row-major.
 // dK/dV and dQ are read-modify-written (+=) by exactly one workgroup each.
+#include <mutex>
 #include <type_traits>
 
 #include "bwd_d128.h"
@@ -507,9 +508,39 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
   }
 }
 
+// Scratch of the split dK/dV kernel: kDkdvScratchBytes of device memory per device,
+// allocated by the first step that splits and kept until the process ends.  Steps
+// on one device share it, so steps that overlap on one device (different streams)
+// must not both split; the ring runs its steps in stream order.
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+ra_status device_scratch(void*& out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(RA_ERR_HIP, "ring_attn_bwd_step: no current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipMalloc(&p, kDkdvScratchBytes) != hipSuccess)
+      return fail(RA_ERR_HIP, "ring_attn_bwd_step: scratch allocation (%zu bytes) failed", kDkdvScratchBytes);
+    g_scratch[dev] = p;
+  }
+  out = g_scratch[dev];
+  return RA_OK;
+}
+
 template <typename T, int D>
 ra_status launch_bwd(BwdArgs args, hipStream_t stream) {
-  if constexpr (std::is_same<T, __bf16>::value && D == 128) return launch_bwd_d128(args, stream);
+  if constexpr (std::is_same<T, __bf16>::value && D == 128) {
+    void* scratch = nullptr;
+    if (bwd_d128_needs_scratch(args)) {
+      const ra_status st = device_scratch(scratch);
+      if (st != RA_OK) return st;
+    }
+    return launch_bwd_d128(args, stream, scratch);
+  }
   // dK/dV: one workgroup per (b, kv head, 128-key tile).
   args.n_tiles = (args.Sk + 32 * kWaves - 1) / (32 * kWaves);
   int64_t n_wg = (int64_t)args.B * args.Hkv * args.n_tiles;
@@ -569,6 +600,9 @@ extern "C" ra_status ring_attn_bwd_step(const ra_shape* s, const void* q, const 
   a.scale = s->softmax_scale;
   a.scale_log2 = s->softmax_scale * kLog2e;
   a.n_tiles = 0;
+  a.part = nullptr;
+  a.count = nullptr;
+  a.n_split = 1;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (s->dtype == RA_DTYPE_BF16) {
     if (s->head_dim == 128) return launch_bwd<__bf16, 128>(a, hs);
