@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     lse_merge,
     ring_attn_bwd_preprocess,
     ring_attn_bwd_step,
+    ring_attn_bwd_step_noalloc,
     ring_attn_fwd_step,
     ring_attn_fwd_step_merge,
     ring_recv_copy,

@@ -27,6 +27,7 @@ EXPORTED = (
     "segment_mask_from_pos",
     "ring_attn_bwd_preprocess",
     "ring_attn_bwd_step",
+    "ring_attn_bwd_step_noalloc",
     "ring_recv_copy",
     "ra_status_string",
     "ra_last_error",
@@ -81,9 +82,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.segment_mask_from_pos.argtypes = [i32, i64, vp, vp, vp]
     lib.ring_attn_bwd_preprocess.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.ring_attn_bwd_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
+    lib.ring_attn_bwd_step_noalloc.argtypes = lib.ring_attn_bwd_step.argtypes
     lib.ring_recv_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
     for fn in ("ring_attn_fwd_step", "ring_attn_fwd_step_merge", "lse_merge", "segment_mask_from_pos", "ring_attn_bwd_preprocess",
-               "ring_attn_bwd_step", "ring_recv_copy"):
+               "ring_attn_bwd_step", "ring_attn_bwd_step_noalloc", "ring_recv_copy"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.ra_status_string.argtypes = [ctypes.c_int]
     lib.ra_status_string.restype = ctypes.c_char_p
@@ -238,9 +240,8 @@ def ring_attn_bwd_preprocess(o, d_o, delta, stream=None) -> None:
                                                                     _ptr(d_o), _ptr(delta), _stream(stream)))
 
 
-def ring_attn_bwd_step(q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, *, q_offset: int, kv_offset: int,
-                       causal: bool, scale: float, seg_ids: Optional[torch.Tensor] = None, stream=None) -> None:
-    """One backward ring step for one KV chunk; accumulates into dq_acc, dk_acc, dv_acc (fp32)."""
+def _bwd_step(fn, q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, q_offset, kv_offset, causal, scale, seg_ids,
+              stream) -> None:
     B, Sq, Hq, d = q.shape
     _need(q, "q", q.shape)
     _need(k, "k", k.shape, q.dtype)
@@ -259,10 +260,24 @@ def ring_attn_bwd_step(q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, *, q_of
         seg_len = seg_ids.shape[1]
     shape = make_shape(q, k, q_offset, kv_offset, causal, scale)
     lib = load()
-    _check("ring_attn_bwd_step", lib.ring_attn_bwd_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o),
-                                                        _ptr(lse), _ptr(delta), _ptr(seg_ids), seg_len,
-                                                        _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc),
-                                                        _stream(stream)))
+    _check(fn, getattr(lib, fn)(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(lse), _ptr(delta),
+                                _ptr(seg_ids), seg_len, _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), _stream(stream)))
+
+
+def ring_attn_bwd_step(q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, *, q_offset: int, kv_offset: int,
+                       causal: bool, scale: float, seg_ids: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One backward ring step for one KV chunk; accumulates into dq_acc, dk_acc, dv_acc (fp32)."""
+    _bwd_step("ring_attn_bwd_step", q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, q_offset, kv_offset, causal,
+              scale, seg_ids, stream)
+
+
+def ring_attn_bwd_step_noalloc(q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, *, q_offset: int, kv_offset: int,
+                               causal: bool, scale: float, seg_ids: Optional[torch.Tensor] = None,
+                               stream=None) -> None:
+    """ring_attn_bwd_step without any device allocation (the library's static scratch;
+    both kernels on `stream`).  Calls that overlap on one GPU must not be issued."""
+    _bwd_step("ring_attn_bwd_step_noalloc", q, k, v, d_o, lse, delta, dq_acc, dk_acc, dv_acc, q_offset, kv_offset,
+              causal, scale, seg_ids, stream)
 
 
 def ring_recv_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

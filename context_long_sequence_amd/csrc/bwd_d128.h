@@ -45,14 +45,23 @@ constexpr size_t kDkdvScratchBytes = kDkdvCountBytes + kDkdvPartBytes;
 constexpr int kD128 = 128;
 constexpr int kD128Tile = 32;  // keys per staged tile of the dQ kernel
 
-// bf16, head_dim 128: dK/dV kernel (bwd_dkdv_d128.hip) then dQ kernel
-// (bwd_dq_d128.hip) on `stream`.  `scratch` (kDkdvScratchBytes, device memory) is
-// used when the 32-key dK/dV kernel splits its key blocks; bwd_d128_needs_scratch
-// tells whether this step does.
-ra_status launch_bwd_d128(BwdArgs args, hipStream_t stream, void* scratch);
+// bf16, head_dim 128: dK/dV kernel (bwd_dkdv_d128.hip) on `stream` and dQ kernel
+// (bwd_dq_d128.hip) on the device's side stream (`side`), or both on `stream`.
+// `scratch` (kDkdvScratchBytes, device memory) is used when the 32-key dK/dV kernel
+// splits its key blocks; bwd_d128_needs_scratch tells whether this step does.
+ra_status launch_bwd_d128(BwdArgs args, hipStream_t stream, void* scratch, bool side);
 bool bwd_d128_needs_scratch(const BwdArgs& args);
 ra_status launch_dkdv_d128(BwdArgs args, hipStream_t stream, void* scratch);
 int dkdv_d128_split(const BwdArgs& args);
+
+// The backward step behind the C entry points (bwd_step.hip): checks, then the
+// kernels.  scratch: device memory of kDkdvScratchBytes or null; when a split step
+// needs scratch and none is given, `allocate` lets it take the device's
+// library-allocated scratch (else the step fails).  side: run dQ on the side stream.
+ra_status bwd_step_entry(const ra_shape* s, const void* q, const void* k, const void* v, const void* d_o,
+                         const float* lse, const float* delta, const int32_t* seg_ids, int64_t seg_len,
+                         float* dq_acc, float* dk_acc, float* dv_acc, void* stream, void* scratch, bool allocate,
+                         bool side);
 // dK/dV with 64 keys per wave (bwd_dkdv64_d128.hip) and its grid size.
 ra_status launch_dkdv64_d128(BwdArgs args, hipStream_t stream);
 int64_t dkdv64_d128_workgroups(const BwdArgs& args);

@@ -606,6 +606,12 @@ ra_status launch_dkdv_d128(BwdArgs args, hipStream_t stream, void* scratch) {
   args.part = nullptr;
   if (args.n_split > 1) {
     if (!scratch) return fail(RA_ERR_INVALID_ARGUMENT, "ring_attn_bwd_step: split dK/dV needs scratch");
+    // The split is sized to the scratch (dkdv_d128_split), so this holds; checked
+    // because the allocation-free entry point's scratch cannot grow.
+    if (n_blk > kDkdvCounters || (size_t)n_wg * kDkdvPartPerWg > kDkdvPartBytes)
+      return fail(RA_ERR_INVALID_ARGUMENT,
+                  "ring_attn_bwd_step: %lld key blocks x %d splits exceed the dK/dV scratch (%zu bytes)",
+                  (long long)n_blk, args.n_split, kDkdvScratchBytes);
     args.count = static_cast<int*>(scratch);
     args.part = reinterpret_cast<float*>(static_cast<char*>(scratch) + kDkdvCountBytes);
     // The arrival counters start at zero (a fill kernel: no memset node in a graph).

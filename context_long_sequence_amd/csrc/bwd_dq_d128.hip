@@ -316,21 +316,30 @@ bool bwd_d128_needs_scratch(const BwdArgs& args) {
   return dkdv64_d128_workgroups(args) < 256 && dkdv_d128_split(args) > 1;
 }
 
-ra_status launch_bwd_d128(BwdArgs args, hipStream_t stream, void* scratch) {
+ra_status launch_bwd_d128(BwdArgs args, hipStream_t stream, void* scratch, bool side) {
+  // dK/dV: 64 keys per wave (half the LDS operand bytes per MFMA) when that grid
+  // still gives each of the 256 CUs a workgroup; 32 keys per wave on small chunks,
+  // with the query tiles of a key block split over two workgroups where the blocks'
+  // work is uneven.  dQ: 64 queries per wave on the same condition.
+  auto dkdv = [&](hipStream_t s) {
+    return dkdv64_d128_workgroups(args) >= 256 ? launch_dkdv64_d128(args, s) : launch_dkdv_d128(args, s, scratch);
+  };
+  auto dq = [&](hipStream_t s) {
+    return dq64_d128_workgroups(args) >= 256 ? launch_dq64_d128(args, s) : launch_dq_d128(args, s);
+  };
+  if (!side) {
+    const ra_status st = dkdv(stream);
+    return st != RA_OK ? st : dq(stream);
+  }
   std::lock_guard<std::mutex> lock(g_side_mutex);
   SideStream* ss = nullptr;
   ra_status st = side_stream_locked(ss);
   if (st != RA_OK) return st;
   if (hipEventRecord(ss->fork, stream) != hipSuccess || hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess)
     return fail(RA_ERR_HIP, "ring_attn_bwd_step: fork to the side stream failed");
-  // dK/dV: 64 keys per wave (half the LDS operand bytes per MFMA) when that grid
-  // still gives each of the 256 CUs a workgroup; 32 keys per wave on small chunks,
-  // with the query tiles of a key block split over up to four workgroups.
-  st = dkdv64_d128_workgroups(args) >= 256 ? launch_dkdv64_d128(args, stream)
-                                           : launch_dkdv_d128(args, stream, scratch);
+  st = dkdv(stream);
   if (st != RA_OK) return st;
-  // dQ: 64 queries per wave on the same condition.
-  st = dq64_d128_workgroups(args) >= 256 ? launch_dq64_d128(args, ss->stream) : launch_dq_d128(args, ss->stream);
+  st = dq(ss->stream);
   if (st != RA_OK) return st;
   if (hipEventRecord(ss->join, ss->stream) != hipSuccess || hipStreamWaitEvent(stream, ss->join, 0) != hipSuccess)
     return fail(RA_ERR_HIP, "ring_attn_bwd_step: join from the side stream failed");

@@ -532,14 +532,14 @@ ra_status device_scratch(void*& out) {
 }
 
 template <typename T, int D>
-ra_status launch_bwd(BwdArgs args, hipStream_t stream) {
+ra_status launch_bwd(BwdArgs args, hipStream_t stream, void* scratch, bool allocate, bool side) {
   if constexpr (std::is_same<T, __bf16>::value && D == 128) {
-    void* scratch = nullptr;
-    if (bwd_d128_needs_scratch(args)) {
+    if (!scratch && bwd_d128_needs_scratch(args)) {
+      if (!allocate) return fail(RA_ERR_INVALID_ARGUMENT, "ring_attn_bwd_step: this step needs scratch");
       const ra_status st = device_scratch(scratch);
       if (st != RA_OK) return st;
     }
-    return launch_bwd_d128(args, stream, scratch);
+    return launch_bwd_d128(args, stream, scratch, side);
   }
   // dK/dV: one workgroup per (b, kv head, 128-key tile).
   args.n_tiles = (args.Sk + 32 * kWaves - 1) / (32 * kWaves);
@@ -565,11 +565,12 @@ ra_status launch_bwd(BwdArgs args, hipStream_t stream) {
 }  // namespace
 }  // namespace ra
 
-extern "C" ra_status ring_attn_bwd_step(const ra_shape* s, const void* q, const void* k, const void* v,
-                                        const void* d_o, const float* lse, const float* delta,
-                                        const int32_t* seg_ids, int64_t seg_len, float* dq_acc, float* dk_acc,
-                                        float* dv_acc, void* stream) {
-  using namespace ra;
+namespace ra {
+
+ra_status bwd_step_entry(const ra_shape* s, const void* q, const void* k, const void* v, const void* d_o,
+                         const float* lse, const float* delta, const int32_t* seg_ids, int64_t seg_len,
+                         float* dq_acc, float* dk_acc, float* dv_acc, void* stream, void* scratch, bool allocate,
+                         bool side) {
   ra_status st = validate_step(s, seg_ids, seg_len);
   if (st != RA_OK) return st;
   if (!q || !k || !v || !d_o || !lse || !delta || !dq_acc || !dk_acc || !dv_acc)
@@ -605,9 +606,19 @@ extern "C" ra_status ring_attn_bwd_step(const ra_shape* s, const void* q, const 
   a.n_split = 1;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (s->dtype == RA_DTYPE_BF16) {
-    if (s->head_dim == 128) return launch_bwd<__bf16, 128>(a, hs);
-    return launch_bwd<__bf16, 64>(a, hs);
+    if (s->head_dim == 128) return launch_bwd<__bf16, 128>(a, hs, scratch, allocate, side);
+    return launch_bwd<__bf16, 64>(a, hs, scratch, allocate, side);
   }
-  if (s->head_dim == 128) return launch_bwd<float, 128>(a, hs);
-  return launch_bwd<float, 64>(a, hs);
+  if (s->head_dim == 128) return launch_bwd<float, 128>(a, hs, scratch, allocate, side);
+  return launch_bwd<float, 64>(a, hs, scratch, allocate, side);
+}
+
+}  // namespace ra
+
+extern "C" ra_status ring_attn_bwd_step(const ra_shape* s, const void* q, const void* k, const void* v,
+                                        const void* d_o, const float* lse, const float* delta,
+                                        const int32_t* seg_ids, int64_t seg_len, float* dq_acc, float* dk_acc,
+                                        float* dv_acc, void* stream) {
+  return ra::bwd_step_entry(s, q, k, v, d_o, lse, delta, seg_ids, seg_len, dq_acc, dk_acc, dv_acc, stream, nullptr,
+                            true, true);
 }

@@ -206,6 +206,24 @@ ra_status ring_attn_bwd_step(const ra_shape* shape, const void* q, const void* k
                              float* dk_acc, float* dv_acc, void* stream);
 
 /*
+ * ring_attn_bwd_step_noalloc — ring_attn_bwd_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, same kernels, bit-identical results; it calls
+ * no allocating routine.
+ * Scratch: the split dK/dV kernel's arrival counters and partial sums live in a
+ * static device array of the library (64 MiB + 256 KiB on each GPU it runs on, held
+ * until the process ends; its address is looked up once per device).  The split is
+ * sized to that array, so no step needs more; the array is shared by every call on
+ * the GPU, so calls that overlap on one GPU (concurrent streams) race and must not
+ * be issued.  Both kernels of the step run on `stream` (no side stream).
+ * Errors: as ring_attn_bwd_step; RA_ERR_HIP if the scratch address lookup fails.
+ */
+ra_status ring_attn_bwd_step_noalloc(const ra_shape* shape, const void* q, const void* k,
+                                     const void* v, const void* d_o, const float* lse,
+                                     const float* delta, const int32_t* seg_ids, int64_t seg_len,
+                                     float* dq_acc, float* dk_acc, float* dv_acc, void* stream);
+
+/*
  * ring_recv_copy — the transfer of one ring step, on one GPU: copies `bytes` bytes
  * from `src` (the buffer that stands for the peer's K/V chunk, or for a travelling
  * dK/dV partial) to `dst` (a receive slot) on `stream`, with the DMA engines
