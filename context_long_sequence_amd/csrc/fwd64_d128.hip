@@ -99,9 +99,19 @@ __global__ __launch_bounds__(64 * kNW) void fwd64_d128_kernel(FwdArgs a) {
     kt_end = max(sb, se);
   }
   const int n_t = kt_end - kt_begin;
-  // Merging a step without a live tile into the running result changes nothing:
-  // unless the merged output is also converted, the workgroup is done.
-  if (n_t <= 0 && a.merge && a.out_kind == 0) return;
+  // A step without a live tile: merged into the running result it changes nothing
+  // (the workgroup is done unless the merged output is also converted); alone it is
+  // O = 0, LSE = -inf.  Either way no Q is loaded and no tile is visited.
+  if (n_t <= 0) {
+    if (a.merge && a.out_kind == 0) return;
+    const f32x16 zero[4] = {};
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qi = qw + 32 * qb + col;
+      if (qi < a.Sq) fwd_epilogue<4>(a, zero, 0.0f, -INFINITY, b, hq, qi, half);
+    }
+    return;
+  }
 
   // Per lane and query block qb: the query q = qw + 32 qb + col, its Q row (B
   // operands; lane = query column, k-slots = d), and the chunk keys it sees,
@@ -138,16 +148,35 @@ __global__ __launch_bounds__(64 * kNW) void fwd64_d128_kernel(FwdArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) asm volatile("" : "+a"(qf[qb][s]));
 
-  // Tiles [m_first, kt_end) may hold an invisible element for some lane of the wave
-  // (the causal diagonal, the chunk's ragged end); every tile does if the wave's
-  // queries run past the shard, and for packed rows.
-  int m_first = kt_begin;
-  if (!kSeg && qw + kQW <= a.Sq) {
-    int64_t first_hidden = a.Sk;  // first chunk key the wave's first query does not see
+  // Tiles that may hold an invisible element for some lane of the wave run the
+  // masked body: [m_first, kt_end) (the causal diagonal, the chunk's ragged end,
+  // for packed rows the end of the wave's sample) and, for packed rows, the tiles
+  // before the first one inside the wave's sample, [kt_begin, kt_begin + n_pre).
+  // Every tile does if the wave's queries run past the shard or, packed, span two
+  // samples.
+  int m_first = kt_begin, n_pre = 0;
+  bool one_row_range = qw + kQW <= a.Sq;
+  int64_t full_lo = 0, full_hi = a.Sk;  // chunk keys that every query of the wave may share a sample with
+  if constexpr (kSeg) {
+    if (one_row_range) {
+      const int s0 = seg_row[a.q_offset + qw];
+      one_row_range = s0 == seg_row[a.q_offset + qw + kQW - 1];
+      if (one_row_range) {
+        int64_t s_lo, s_hi;
+        seg_span(seg_row, a.seg_len, s0, s_lo, s_hi);
+        full_lo = s_lo - a.kv_offset;
+        full_hi = s_hi - a.kv_offset;
+      }
+    }
+  }
+  if (one_row_range) {
+    int64_t first_hidden = min<int64_t>(a.Sk, full_hi);  // first chunk key some query may not see
     if (a.causal) first_hidden = min<int64_t>(first_hidden, a.q_offset + qw - a.kv_offset + 1);
     int64_t mt = max<int64_t>(0, first_hidden) / kKT;  // tile holding it
     if (a.Sk % kKT != 0) mt = min<int64_t>(mt, a.Sk / kKT);
     m_first = (int)max<int64_t>(kt_begin, min<int64_t>(kt_end, mt));
+    const int64_t first_full = (max<int64_t>(0, full_lo) + kKT - 1) / kKT;  // first tile inside the sample
+    n_pre = (int)max<int64_t>(0, min<int64_t>(n_t, first_full - kt_begin));
   }
 
   f32x16 oacc[2][4];
@@ -399,12 +428,22 @@ __global__ __launch_bounds__(64 * kNW) void fwd64_d128_kernel(FwdArgs a) {
   // fills slot t % 4 with tile t+4.  Iterations whose tile t may need the element
   // mask run the masked body; they start at a multiple of four (up to three more
   // run masked: correct, only slower) so that both loops start at slot 0.
-  const int first_m_it = m_first - kt_begin;
-  const int n_plain = min(n_t, first_m_it / 4 * 4);
+  // Loops in whole groups of four iterations, so that each starts at slot 0: a
+  // masked prefix (rounded up: more masked iterations are correct, only slower),
+  // the unmasked middle, the masked rest.
+  const int pre4 = min(n_t, (n_pre + 3) / 4 * 4);
+  const int end_plain = max(pre4, (m_first - kt_begin) / 4 * 4);
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   int t = 0;
-  for (; t < n_plain; t += 4) {
+  for (; t < pre4; t += 4) {
+    const BoolTag<true> mk;
+    iteration(mk, P0{}, t, ks1, vs0, ks2, ks0, vs0, okn);
+    if (t + 1 < n_t) iteration(mk, P1{}, t + 1, ks2, vs1, ks3, ks1, vs1, okn);
+    if (t + 2 < n_t) iteration(mk, P0{}, t + 2, ks3, vs2, ks0, ks2, vs2, okn);
+    if (t + 3 < n_t) iteration(mk, P1{}, t + 3, ks0, vs3, ks1, ks3, vs3, okn);
+  }
+  for (; t < end_plain; t += 4) {
     const BoolTag<false> um;
     iteration(um, P0{}, t, ks1, vs0, ks2, ks0, vs0, okn);
     iteration(um, P1{}, t + 1, ks2, vs1, ks3, ks1, vs1, okn);

@@ -59,6 +59,11 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, const f32x16 (&oa
     return;
   }
   const MergeWeights mw = merge_weights(a.lse[li], ls);
+  // A row this step adds nothing to (weight 0: merge_o returns the running O and the
+  // merged LSE equals the running one, bit for bit) is left as it is: only read, and
+  // only when it is also converted.
+  const bool changed = mw.live && mw.ws != 0.0f;
+  if (!changed && a.out_kind == 0) return;
   f32x4 o[DB][4];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -69,7 +74,7 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, const f32x16 (&oa
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int c = 32 * db + 8 * r4 + 4 * half;
-      if (mw.live) {
+      if (changed) {
         o[db][r4] = merge_o(o[db][r4], os[db][r4], mw);
         *reinterpret_cast<f32x4*>(orow + c) = o[db][r4];
       }
@@ -78,7 +83,7 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, const f32x16 (&oa
       else if (a.out_kind == 2)
         *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.o_out) + row + c) = to_bf16x4(o[db][r4]);
     }
-  if (half == 0 && mw.live) a.lse[li] = mw.lse;
+  if (half == 0 && changed) a.lse[li] = mw.lse;
 }
 
 // bf16, head_dim 128, 64 queries per wave (fwd64_d128.hip): grid size and launch.
