@@ -355,6 +355,29 @@ def packed_live_pairs(lengths, C, rank):
     return total
 
 
+def packed_executed_pairs(np, seg_row, C, rank, cp, qblock=64, ktile=32):
+    """(query, key) pairs the packed forward computes per query head: for every block
+    of `qblock` local queries and every chunk, the key tiles of `ktile` keys from the
+    first to the last that shares a sample with the block, within the causal range
+    (the forward kernel's tile range on packed rows).  seg_row: the row's segment ids."""
+    total = 0
+    for c in range(cp):
+        for q0 in range(0, C, qblock):
+            q_last = min(q0 + qblock, C) - 1
+            n_keys = max(0, min(C, rank * C + q_last - c * C + 1))
+            n_tiles = (n_keys + ktile - 1) // ktile
+            if n_tiles == 0:
+                continue
+            lo, hi = seg_row[rank * C + q0], seg_row[rank * C + q_last]
+            starts = c * C + np.arange(n_tiles) * ktile
+            ends = c * C + np.minimum(np.arange(1, n_tiles + 1) * ktile, C) - 1
+            live = (seg_row[ends] >= lo) & (seg_row[starts] <= hi)
+            idx = np.nonzero(live)[0]
+            if idx.size:
+                total += qblock * ktile * int(idx[-1] - idx[0] + 1)
+    return total
+
+
 def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_workload):
     """Forward TFLOP/s of the 8K and packed-16K shares, the segment-id kernel time, the
     load-balanced (zigzag) 64K forward+backward of ranks 0 and 7, the 64K ring with
@@ -428,8 +451,10 @@ def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_wor
     bms = ev_ms(lambda: ra.ring_backward(q, ks, vs, o4, l4, do, c4.rank, c4.CP, causal=True, seg_ids=seg,
                                          delta=ws.delta, **zeroed(g4)))
     pairs4 = packed_live_pairs(wl.lengths, c4.C, c4.rank)
+    exec4 = packed_executed_pairs(np, seg[0].cpu().numpy(), c4.C, c4.rank, c4.CP)
     out["packed_16k_cp4_r2"] = {
         "live_pairs": pairs4, "frac_of_causal_pairs": round(pairs4 / live_pairs_causal(c4.C, c4.rank), 4),
+        "fwd_executed_pairs": exec4, "live_frac_of_executed": round(pairs4 / exec4, 4),
         "segment_ids_us": round(seg_ms * 1e3, 2),
         "fwd_ms": round(fms, 4), "fwd_tflops": round(4.0 * c4.Hq * c4.d * pairs4 / (fms * 1e-3) / 1e12, 2),
         "bwd_ms": round(bms, 4), "bwd_tflops": round(10.0 * c4.Hq * c4.d * pairs4 / (bms * 1e-3) / 1e12, 2)}

@@ -198,7 +198,16 @@ ra_status ring_attn_bwd_preprocess(int32_t batch, int32_t q_len, int32_t heads_q
  *  dq_acc [B, Sq, Hq, d] fp32, dk_acc / dv_acc [B, Sk, Hkv, d] fp32: accumulated
  *  with +=; the caller zeroes them before the first step.
  * Masks and seg_ids exactly as in ring_attn_fwd_step.
- * Errors: as ring_attn_fwd_step.
+ * Resources (bf16, head_dim 128): the dQ kernel runs on a side stream of the device
+ * (created on first use, default priority) that joins `stream` before the call's
+ * work is complete in `stream` order; a step whose dK/dV key blocks are split
+ * (causal diagonal chunk or packed rows on small grids) uses 64 MiB + 256 KiB of
+ * device scratch, allocated on the device by the first such step and kept until the
+ * process ends.  Steps that overlap on one device (concurrent streams) must not
+ * both split.  Results are deterministic: split partial sums are added in a fixed
+ * order.
+ * Errors: as ring_attn_fwd_step; RA_ERR_HIP if the side stream or the scratch cannot
+ * be created.
  */
 ra_status ring_attn_bwd_step(const ra_shape* shape, const void* q, const void* k, const void* v,
                              const void* d_o, const float* lse, const float* delta,
