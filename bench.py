@@ -154,9 +154,9 @@ def main():
     del wl
     o = torch.empty_like(q)
     lse = torch.empty((1, cfg.Hq, C), dtype=torch.float32, device=dev)
-    dq = torch.empty((1, C, cfg.Hq, cfg.d), dtype=torch.float32, device=dev)
-    dks = [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in ks]
-    dvs = [torch.empty(v.shape, dtype=torch.float32, device=dev) for v in vs]
+    # dQ and the per-chunk dK/dV accumulators as views of one buffer, cleared by one fill
+    grads = flat_grads(torch, dev, q.shape, [k.shape for k in ks])
+    dq, dks, dvs = grads["dq"], grads["dk_chunks"], grads["dv_chunks"]
     torch.cuda.synchronize()
     base_alloc = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
@@ -169,11 +169,7 @@ def main():
         if args.only in ("fwd", "all"):
             ra.ring_forward(q, ks, vs, r, CP, causal=True, out=o, lse=lse, workspace=ws, step_hook=hook)
         if args.only in ("bwd", "all"):
-            dq.zero_()
-            for x in dks:
-                x.zero_()
-            for x in dvs:
-                x.zero_()
+            grads["flat"].zero_()
             if hook:
                 hook("zero_grads", 0)
             ra.ring_backward(q, ks, vs, o, lse, do, r, CP, causal=True, dq=dq, dk_chunks=dks, dv_chunks=dvs,
@@ -355,6 +351,21 @@ def packed_live_pairs(lengths, C, rank):
     return total
 
 
+def flat_grads(torch, dev, q_shape, kv_shapes):
+    """fp32 dQ [q_shape] and dK/dV [kv_shapes[c]] per chunk as contiguous views of one
+    buffer ("flat"), so that one fill clears them all."""
+    n_q = math.prod(q_shape)
+    n_kv = [math.prod(s) for s in kv_shapes]
+    flat = torch.empty(n_q + 2 * sum(n_kv), dtype=torch.float32, device=dev)
+    out = {"flat": flat, "dq": flat[:n_q].view(q_shape), "dk_chunks": [], "dv_chunks": []}
+    off = n_q
+    for name in ("dk_chunks", "dv_chunks"):
+        for s, n in zip(kv_shapes, n_kv):
+            out[name].append(flat[off:off + n].view(s))
+            off += n
+    return out
+
+
 def packed_executed_pairs(np, seg_row, C, rank, cp, qblock=64, ktile=32):
     """(query, key) pairs the packed forward computes per query head: for every block
     of `qblock` local queries and every chunk, the key tiles of `ktile` keys from the
@@ -401,17 +412,13 @@ def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_wor
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
 
     def grad_buffers(q, ks):
-        """fp32 dQ and per-chunk dK/dV accumulators, allocated once."""
-        return {"dq": torch.empty(q.shape, dtype=torch.float32, device=dev),
-                "dk_chunks": [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in ks],
-                "dv_chunks": [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in ks]}
+        """fp32 dQ and per-chunk dK/dV accumulators, allocated once (views of one buffer)."""
+        return flat_grads(torch, dev, q.shape, [k.shape for k in ks])
 
     def zeroed(gb):
         """Clears the accumulators (part of each timed backward, as in the main step)."""
-        gb["dq"].zero_()
-        for x in gb["dk_chunks"] + gb["dv_chunks"]:
-            x.zero_()
-        return gb
+        gb["flat"].zero_()
+        return {k: gb[k] for k in ("dq", "dk_chunks", "dv_chunks")}
 
     # 8K Llama-3-8B-shaped share (rank 3 of 4), forward
     c2 = LLAMA3_8K_FWD
