@@ -141,6 +141,9 @@ __global__ __launch_bounds__(64 * kNW) void dkdv64_d128_kernel(BwdArgs a) {
   // are nondecreasing, so the queries of one segment are contiguous).  32-bit:
   // offsets clamped to +-2^30, q0 <= 2^30.  A key past the chunk end sees nothing.
   int vis_lo[2], vis_hi[2];
+  SegSpans wsp{};  // the segments of the wave's first and last key
+  if constexpr (kSeg)
+    wsp = seg_spans_wave(seg_row, a.seg_len, a.kv_offset + min(kw, a.Sk - 1), a.kv_offset + min(kw + 64, a.Sk) - 1);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int64_t kgl = a.kv_offset + kw + 32 * kb + col;
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(64 * kNW) void dkdv64_d128_kernel(BwdArgs a) {
     if constexpr (kSeg) {
       if (k_valid[kb]) {
         int64_t s_lo, s_hi;
-        seg_span(seg_row, a.seg_len, seg_row[kgl], s_lo, s_hi);
+        seg_span_lane(seg_row, a.seg_len, wsp, seg_row[kgl], s_lo, s_hi);
         lo = max(lo, s_lo);
         hi = min(hi, s_hi);
       }

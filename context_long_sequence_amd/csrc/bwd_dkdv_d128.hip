@@ -97,8 +97,8 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     seg_k = k_valid ? seg_row[kgl] : INT32_MIN;
     const int lo = seg_row[a.kv_offset + k0], hi = seg_row[a.kv_offset + k_last];
     if (lo == hi) {
-      int64_t sp_lo, sp_hi;  // the segment's token span in the row
-      seg_span(seg_row, a.seg_len, lo, sp_lo, sp_hi);
+      const SegSpans w = seg_spans_wave(seg_row, a.seg_len, a.kv_offset + k0, a.kv_offset + k0);
+      const int64_t sp_lo = w.lo0, sp_hi = w.hi0;  // the segment's token span in the row
       full_lo = max<int64_t>(0, sp_lo - a.q_offset + QT - 1) / QT;
       full_hi = min<int64_t>(n_qt, max<int64_t>(0, sp_hi - a.q_offset) / QT);
       one_seg = true;

@@ -106,6 +106,9 @@ __global__ __launch_bounds__(64 * kNW) void dq64_d128_kernel(BwdArgs a) {
   float neg_lse2[2];
   f32x16 ndl[2];
   int vlo[2], vhi[2];
+  SegSpans wsp{};  // the segments of the wave's first and last query
+  if constexpr (kSeg)
+    wsp = seg_spans_wave(seg_row, a.seg_len, a.q_offset + min(qw, a.Sq - 1), a.q_offset + min(qw + kQW, a.Sq) - 1);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qi = qw + 32 * qb + col;
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(64 * kNW) void dq64_d128_kernel(BwdArgs a) {
     if constexpr (kSeg) {
       if (qv) {
         int64_t s_lo, s_hi;
-        seg_span(seg_row, a.seg_len, seg_row[qg], s_lo, s_hi);
+        seg_span_lane(seg_row, a.seg_len, wsp, seg_row[qg], s_lo, s_hi);
         lo = max<int64_t>(lo, s_lo - a.kv_offset);
         hi = min<int64_t>(hi, s_hi - 1 - a.kv_offset);
       }

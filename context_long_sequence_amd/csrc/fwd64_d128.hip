@@ -119,6 +119,9 @@ __global__ __launch_bounds__(64 * kNW) void fwd64_d128_kernel(FwdArgs a) {
   // a query past the shard sees nothing.
   bf16x8 qf[2][8];
   int vlo[2], vhi[2];
+  SegSpans wsp{};  // the segments of the wave's first and last query
+  if constexpr (kSeg)
+    wsp = seg_spans_wave(seg_row, a.seg_len, a.q_offset + min(qw, a.Sq - 1), a.q_offset + min(qw + kQW, a.Sq) - 1);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qi = qw + 32 * qb + col;
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(64 * kNW) void fwd64_d128_kernel(FwdArgs a) {
     if constexpr (kSeg) {
       if (qv) {
         int64_t s_lo, s_hi;
-        seg_span(seg_row, a.seg_len, seg_row[qg], s_lo, s_hi);
+        seg_span_lane(seg_row, a.seg_len, wsp, seg_row[qg], s_lo, s_hi);
         lo = max<int64_t>(lo, s_lo - a.kv_offset);
         hi = min<int64_t>(hi, s_hi - 1 - a.kv_offset);
       }
@@ -158,16 +161,9 @@ __global__ __launch_bounds__(64 * kNW) void fwd64_d128_kernel(FwdArgs a) {
   bool one_row_range = qw + kQW <= a.Sq;
   int64_t full_lo = 0, full_hi = a.Sk;  // chunk keys that every query of the wave may share a sample with
   if constexpr (kSeg) {
-    if (one_row_range) {
-      const int s0 = seg_row[a.q_offset + qw];
-      one_row_range = s0 == seg_row[a.q_offset + qw + kQW - 1];
-      if (one_row_range) {
-        int64_t s_lo, s_hi;
-        seg_span(seg_row, a.seg_len, s0, s_lo, s_hi);
-        full_lo = s_lo - a.kv_offset;
-        full_hi = s_hi - a.kv_offset;
-      }
-    }
+    one_row_range = one_row_range && wsp.s0 == wsp.s1;
+    full_lo = wsp.lo0 - a.kv_offset;
+    full_hi = wsp.hi0 - a.kv_offset;
   }
   if (one_row_range) {
     int64_t first_hidden = min<int64_t>(a.Sk, full_hi);  // first chunk key some query may not see

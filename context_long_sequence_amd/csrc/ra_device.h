@@ -293,6 +293,66 @@ __device__ __forceinline__ void seg_tile_range(const int32_t* row, int n, int ti
   out_end = last + 1;
 }
 
+// Token spans of the segments of a wave's tokens [t_first, t_last] of a row of `n`
+// nondecreasing segment ids: the segments s0 of t_first and s1 of t_last, and their
+// spans [lo0, hi0), [lo1, hi1).  Wave-collective (call with every lane active and
+// wave-uniform arguments): the four bounds are found by 64-way searches run side by
+// side, in which each lane tests one point of the remaining range per round -- a few
+// dependent rounds of loads instead of a binary search's one load per halving.
+struct SegSpans {
+  int s0, s1;
+  int64_t lo0, hi0, lo1, hi1;
+};
+__device__ __forceinline__ SegSpans seg_spans_wave(const int32_t* row, int64_t n, int64_t t_first, int64_t t_last) {
+  const int lane = threadIdx.x & 63;
+  SegSpans r;
+  r.s0 = row[t_first];
+  r.s1 = row[t_last];
+  // bound k is the first index whose id is >= s (k even) or > s (k odd), s = s0 for
+  // k < 2, s1 otherwise; it lies in [L[k], H[k]], narrowed by the tokens themselves.
+  int64_t L[4] = {0, t_first + 1, 0, t_last + 1};
+  int64_t H[4] = {t_first, n, t_last, n};
+  for (int round = 0; round < 12; ++round) {
+    bool active = false;
+    int64_t step[4], p[4];
+    int v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      active |= L[k] < H[k];
+      step[k] = (H[k] - L[k] + 63) / 64;
+      p[k] = L[k] + (int64_t)lane * step[k];
+    }
+    if (!active) break;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = (L[k] < H[k] && p[k] < H[k]) ? row[p[k]] : 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (L[k] >= H[k]) continue;
+      const int sk = k < 2 ? r.s0 : r.s1;
+      const bool t = p[k] >= H[k] || ((k & 1) ? v[k] > sk : v[k] >= sk);
+      const uint64_t m = __ballot(t);
+      if (m == 0) {
+        L[k] = L[k] + 63 * step[k] + 1;  // past the last point tested
+      } else {
+        const int j = (int)__builtin_ctzll(m);
+        const int64_t hj = L[k] + (int64_t)j * step[k];
+        if (j == 0) {
+          H[k] = L[k];
+        } else {
+          const int64_t l_new = L[k] + (int64_t)(j - 1) * step[k] + 1;
+          H[k] = hj < H[k] ? hj : H[k];
+          L[k] = l_new;
+        }
+      }
+    }
+  }
+  r.lo0 = L[0];
+  r.hi0 = L[1];
+  r.lo1 = L[2];
+  r.hi1 = L[3];
+  return r;
+}
+
 // Token span [lo, hi) of segment `s` in a row of `n` nondecreasing segment ids:
 // lo = first index with id >= s, hi = first index with id > s (binary searches).
 // With ids that decrease somewhere the span is some range inside [0, n] (never an
@@ -316,6 +376,22 @@ __device__ __forceinline__ void seg_span(const int32_t* row, int64_t n, int s, i
       b = m;
   }
   hi = a;
+}
+
+// The span [lo, hi) of segment `s` of one of the wave's tokens, from the wave's
+// spans when s is the segment of its first or last token, else by seg_span (a block
+// of three or more samples).
+__device__ __forceinline__ void seg_span_lane(const int32_t* row, int64_t n, const SegSpans& w, int s, int64_t& lo,
+                                              int64_t& hi) {
+  if (s == w.s0) {
+    lo = w.lo0;
+    hi = w.hi0;
+  } else if (s == w.s1) {
+    lo = w.lo1;
+    hi = w.hi1;
+  } else {
+    seg_span(row, n, s, lo, hi);
+  }
 }
 
 }  // namespace ra
