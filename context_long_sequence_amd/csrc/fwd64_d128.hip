@@ -1,6 +1,7 @@
-// ring_attn_fwd_step for the hot shape (bf16, head_dim 128), wide variant: each
-// wave owns 64 queries (two 32-query MFMA blocks), so every K and V operand it
-// reads from LDS feeds two MFMAs -- half the LDS bytes per MFMA of a 32-query wave.
+// ring_attn_fwd_step for the hot shape (bf16, head_dim 128) on packed rows, wide
+// grids: each wave owns 64 queries (two 32-query MFMA blocks), so every K and V
+// operand it reads from LDS feeds two MFMAs -- half the LDS bytes per MFMA of a
+// 32-query wave.
 //   s_ij = scale * q_i . k_j over the visible keys of this chunk,
 //   O_i = sum_j softmax_j(s_ij) v_j,  LSE_i = ln sum_j exp(s_ij)
 // (axolotl docs "Sequence Parallelism", Implementation Details; aicassindra

@@ -651,9 +651,9 @@ ra_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
   if (n_wg > INT32_MAX) return fail(RA_ERR_INVALID_ARGUMENT, "too many workgroups");
   if constexpr (std::is_same<T, __bf16>::value && D == 128) {
     // Packed rows: 64 queries per wave (four query heads of a GQA group per
-    // workgroup) when that grid gives every CU (256 on MI355X) two workgroups.
-    // Measured on a packed 16K share: 0.42 ms against 0.45 ms for the 32-query
-    // kernel; on unpacked rows the 8-wave kernel below is as fast or faster.
+    // workgroup) when that grid gives every CU (256 on MI355X) two workgroups: each
+    // K/V operand read feeds two MFMAs.  On unpacked rows the 8-wave kernel below,
+    // with two waves per SIMD to hide the softmax, is as fast or faster.
     if (args.seg != nullptr && fwd64_d128_workgroups(args) >= 2 * 256) return launch_fwd64_d128(args, stream);
     // 8-wave workgroups when the grid still gives every CU (256 on MI355X) four of
     // them and no segment test runs (packed rows keep the finer 128-query tiles).
