@@ -186,6 +186,14 @@ LONG_SEG_CASES = [
     ("bf16", 1, 1024, 1024, 32, 8, 128, 1024, 1024, True, (300, 1200)),  # diagonal chunk
     ("bf16", 2, 1000, 1100, 16, 4, 128, 1100, 0, True, (150, 900)),     # ragged tails
 ]
+# Long samples on the wide grids: the forward's 64-query waves (unmasked tiles inside
+# a sample), the 64-key dK/dV and 64-query dQ waves (sample spans from wave-wide
+# searches).
+WIDE_LONG_SEG_CASES = [
+    ("bf16", 1, 4096, 2048, 32, 8, 128, 4096, 2048, True, (300, 1500)),  # forward, diagonal chunk
+    ("bf16", 1, 512, 1024, 128, 64, 128, 512, 0, True, (300, 1500)),     # dK/dV 64 keys per wave
+    ("bf16", 2, 512, 2048, 64, 16, 128, 1536, 0, True, (300, 1500)),     # dQ 64 queries per wave
+]
 
 
 def _step_case(case, seed):
@@ -198,7 +206,8 @@ def _step_case(case, seed):
     return q, k, v, seg, S
 
 
-@pytest.mark.parametrize("case", STEP_CASES + WIDE_FWD_CASES + LONG_SEG_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case", STEP_CASES + WIDE_FWD_CASES + LONG_SEG_CASES + WIDE_LONG_SEG_CASES[:1],
+                         ids=lambda c: "-".join(map(str, c)))
 def test_fwd_step_partial(case):
     ra = lib()
     dtype, B, Sq, Sk, Hq, Hkv, d, q_off, kv_off, causal, packed = case
@@ -226,7 +235,8 @@ def test_fwd_step_partial(case):
     assert np.all(on[np.transpose(dead, (0, 2, 1))] == 0)
 
 
-@pytest.mark.parametrize("case", STEP_CASES + WIDE_BWD_CASES + LONG_SEG_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case", STEP_CASES + WIDE_BWD_CASES + LONG_SEG_CASES + WIDE_LONG_SEG_CASES[1:],
+                         ids=lambda c: "-".join(map(str, c)))
 def test_bwd_step(case):
     """One backward step with the oracle's own final LSE/delta as inputs: dQ, dK, dV."""
     ra = lib()
