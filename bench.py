@@ -425,7 +425,7 @@ def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_wor
     wl = make_workload(c2, q_chunks=[c2.rank])
     q, ks, vs = bf(wl.q_local), [bf(k) for k in wl.k_chunks], [bf(v) for v in wl.v_chunks]
     ws = ra.RingWorkspace(1, c2.C, c2.Hq, c2.d, dev)
-    ms = ev_ms(lambda: ra.ring_forward(q, ks, vs, c2.rank, c2.CP, causal=True, workspace=ws))
+    ms = ev_ms(lambda: ra.ring_forward(q, ks, vs, c2.rank, c2.CP, causal=True, workspace=ws), reps=20)
     pairs = live_pairs_causal(c2.C, c2.rank)
     out["fwd_8k_cp4_r3"] = {"ms": round(ms, 4), "tflops": round(4.0 * c2.Hq * c2.d * pairs / (ms * 1e-3) / 1e12, 2)}
     # the same share's backward (dO ~ N(0,1)), from the forward's O and LSE
@@ -436,7 +436,7 @@ def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_wor
     do2 = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(5), device=dev).to(torch.bfloat16)
     g2 = grad_buffers(q, ks)
     bms = ev_ms(lambda: ra.ring_backward(q, ks, vs, o2, l2, do2, c2.rank, c2.CP, causal=True, delta=ws.delta,
-                                         **zeroed(g2)))
+                                         **zeroed(g2)), reps=20)
     out["bwd_8k_cp4_r3"] = {"ms": round(bms, 4),
                             "tflops": round(10.0 * c2.Hq * c2.d * pairs / (bms * 1e-3) / 1e12, 2)}
     del o2, l2, do2
@@ -453,10 +453,10 @@ def side_measurements(torch, ra, np, dev, LLAMA3_8K_FWD, PACKED16K_FWD, make_wor
     o4 = torch.empty_like(q)
     l4 = torch.empty((1, c4.Hq, c4.C), dtype=torch.float32, device=dev)
     fms = ev_ms(lambda: ra.ring_forward(q, ks, vs, c4.rank, c4.CP, causal=True, seg_ids=seg, workspace=ws,
-                                         out=o4, lse=l4))
+                                         out=o4, lse=l4), reps=20)
     g4 = grad_buffers(q, ks)
     bms = ev_ms(lambda: ra.ring_backward(q, ks, vs, o4, l4, do, c4.rank, c4.CP, causal=True, seg_ids=seg,
-                                         delta=ws.delta, **zeroed(g4)))
+                                         delta=ws.delta, **zeroed(g4)), reps=20)
     pairs4 = packed_live_pairs(wl.lengths, c4.C, c4.rank)
     exec4 = packed_executed_pairs(np, seg[0].cpu().numpy(), c4.C, c4.rank, c4.CP)
     out["packed_16k_cp4_r2"] = {
