@@ -558,8 +558,21 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
         const bf16x4_t x1 = tr_read(vb + (vB1 ^ (db << 6)) + 2048 * m);
         vf[db] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
+      // Two waves share each SIMD.  With 4-wave workgroups (two per CU) the products
+      // go out at raised priority, ahead of the other wave's softmax instructions
+      // (8K chunk step -2 to -7 %); with 8-wave workgroups each group of four stays
+      // together in the schedule (64K chunk step -1 %), where the priority gained
+      // nothing.
+      if constexpr (NW == 4)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] = mfma_bf16(vf[db], m ? pf1 : pf0, oacc[db]);
+      if constexpr (NW == 4)
+        __builtin_amdgcn_s_setprio(0);
+      else
+        __builtin_amdgcn_sched_barrier(0);
     }
   };
 
