@@ -201,32 +201,60 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     const int row = (4 * wave + r) * 4 + (lane >> 4);
     coff[r] = (uint32_t)(row * q_rb + ((lane & 15) ^ swz(row)) * 16);
   }
-  auto issue = [&](__bf16* qs, __bf16* ds, float* xs) {
+  // A tile's copies are planned once (walk step, addresses, ranges) and issued in
+  // two parts: the per-query row right after the barrier that frees its slot, the
+  // eight 1 KiB row blocks one per MFMA pair in the first phase of the step, instead
+  // of nine back to back.  A plan past the last tile has empty ranges: its loads
+  // read nothing and write zeros into the free slot.
+  struct CopyPlan {
+    const char* q;
+    const char* d;
+    const char* x;
+    int bytes, xbytes;
+  };
+  auto plan_copy = [&](bool valid) {
     int hq, qt;
     walk_tile(issue_walk, hq, qt);
     walk_next(issue_walk);
-    const int q0 = qt * QT;
-    const int rows = min(a.Sq - q0, QT);  // >= 1; the descriptors end at the tile's last valid row
-    const int64_t hoff = (int64_t)q0 * q_rb + (int64_t)hq * (kD * 2);
-    const int bytes = (rows - 1) * q_rb + kD * 2;  // < 2^31: q_rb <= 4096 * 256
-    const buffer_rsrc rq = make_rsrc32(qg_base + hoff, bytes);
-    const buffer_rsrc rd = make_rsrc32(dg_base + hoff, bytes);
-    char* dq_ = reinterpret_cast<char*>(qs) + 4 * wave * 1024;
-    char* dd_ = reinterpret_cast<char*>(ds) + 4 * wave * 1024;
-    // The per-query row first: wave 0 rescales its LSE row one step later and
-    // waits for this copy alone.
-    const int64_t li = ((int64_t)b * a.Hq + hq) * a.Sq + q0;
-    const void* src = a.lse + li;
-    if (wave == 1) src = a.delta + li;
-    if constexpr (kSeg) {
-      if (wave == 2) src = seg_row + a.q_offset + q0;
+    CopyPlan p{qg_base, dg_base, reinterpret_cast<const char*>(a.lse), 0, 0};
+    if (valid) {
+      const int q0 = qt * QT;
+      const int rows = min(a.Sq - q0, QT);  // >= 1; the descriptors end at the tile's last valid row
+      const int64_t hoff = (int64_t)q0 * q_rb + (int64_t)hq * (kD * 2);
+      // The per-query row: LSE (wave 0), delta (wave 1), segment ids (wave 2), or
+      // the LSE again as a dummy (wave 3).
+      const int64_t li = ((int64_t)b * a.Hq + hq) * a.Sq + q0;
+      const void* src = a.lse + li;
+      if (wave == 1) src = a.delta + li;
+      if constexpr (kSeg) {
+        if (wave == 2) src = seg_row + a.q_offset + q0;
+      }
+      p.q = qg_base + hoff;
+      p.d = dg_base + hoff;
+      p.x = static_cast<const char*>(src);
+      p.bytes = (rows - 1) * q_rb + kD * 2;  // < 2^31: q_rb <= 4096 * 256
+      p.xbytes = rows * 4;
     }
-    buffer_load_lds4(make_rsrc32(src, rows * 4), xs + wave * QT, (uint32_t)lane * 4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) buffer_load_lds16(rq, dq_ + r * 1024, coff[r]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) buffer_load_lds16(rd, dd_ + r * 1024, coff[r]);
+    return p;
   };
+  // The per-query row first: wave 0 rescales its LSE row one step later and waits
+  // for this copy alone.
+  auto issue_row = [&](const CopyPlan& p, float* xs) {
+    buffer_load_lds4(make_rsrc32(p.x, p.xbytes), xs + wave * QT, (uint32_t)lane * 4);
+  };
+  // Row block r of the tile: Q blocks 4w .. 4w+3 (r = 0..3), dO blocks (r = 4..7).
+  auto issue_block = [&](const CopyPlan& p, int r, __bf16* qs, __bf16* ds) {
+    char* dst = reinterpret_cast<char*>(r < 4 ? qs : ds) + (4 * wave + (r & 3)) * 1024;
+    buffer_load_lds16(make_rsrc32(r < 4 ? p.q : p.d, p.bytes), dst, coff[r & 3]);
+  };
+  auto issue = [&](const CopyPlan& p, __bf16* qs, __bf16* ds, float* xs) {
+    issue_row(p, xs);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) issue_block(p, r, qs, ds);
+  };
+  CopyPlan pend{};  // the tile whose row blocks the step's first phase issues
+  __bf16* pend_q = nullptr;
+  __bf16* pend_d = nullptr;
   constexpr int kCopiesPerTile = 9;
   static_assert(kCopiesPerTile == 2 * (QT / 4 / 4) + 1, "copy count per wave and tile");
 
@@ -237,8 +265,9 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   // tile t+2) and writes it back after step t's arithmetic; the barrier of step t+1
   // publishes it.  Saves 32 multiplications per lane and tile in the other waves.
   auto rescale_wait = [&](bool next2) {
+    // Tile it+1's row was followed by its 8 row blocks and tile it+2's row (if any).
     if (next2)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(17));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
     else
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
   };
@@ -371,6 +400,7 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
       fq[1][c] = load_bf16x8(qc + 8192 + (rA ^ (c << 5)));
       if (c == 2) read_rows(0);
       if (c == 5) read_delta(1);
+      issue_block(pend, c, pend_q, pend_d);  // tile it+2 (empty ranges past the last tile)
       fence();
       dp[0] = mfma_bf16(fd[0][c], vf[c], c == 0 ? dlv[0] : dp[0]);
       fd[1][c] = load_bf16x8(dc + 8192 + (rA ^ (c << 5)));
@@ -447,7 +477,10 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (it + 2 < len) issue(qn, dn, xn);
+    pend = plan_copy(it + 2 < len);
+    pend_q = qn;
+    pend_d = dn;
+    if (it + 2 < len) issue_row(pend, xn);
     const bool resc = wave == 0 && it + 1 < len;
     float lraw = 0.0f;
     if (resc) {
@@ -462,8 +495,8 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   };
 
   // Steps it = 0 .. len-1 visit positions p_begin + it.
-  issue(qs0, ds0, xs0);
-  if (len > 1) issue(qs1, ds1, xs1);
+  issue(plan_copy(true), qs0, ds0, xs0);
+  if (len > 1) issue(plan_copy(true), qs1, ds1, xs1);
   if (wave == 0) {
     rescale_wait(len > 1);
     xs0[lane] = xs0[lane] * -kLog2e;
