@@ -166,6 +166,16 @@ WIDE_BWD_CASES = [
     ("bf16", 2, 500, 2000, 64, 16, 128, 0, 3000, True, False),    # chunk in the future
 ]
 
+# Backward steps whose dK/dV workgroups (32 keys per wave) walk only 1, 2 or 3 query
+# tiles, so that the copy pipeline runs its prologue alone or one or two loop steps
+# (copies planned past the last tile have empty ranges).
+SHORT_WALK_BWD_CASES = [
+    ("bf16", 1, 64, 256, 2, 2, 128, 0, 0, False, False),      # 1 tile per workgroup
+    ("bf16", 1, 128, 200, 2, 2, 128, 0, 0, False, False),     # 2 tiles, ragged key tail
+    ("bf16", 1, 150, 128, 4, 4, 128, 0, 0, False, False),     # 3 tiles, ragged query tail
+    ("bf16", 2, 64, 64, 8, 2, 128, 64, 64, True, False),      # diagonal, 4 positions (GQA 4:1)
+]
+
 # Forward steps on grids of 512 or more workgroups of 64-query waves (B * Hkv * (group
 # / h) * ceil(Sq / (256 / h)), h = 4, 2 or 1 query heads per workgroup by the GQA
 # group): the size at which the bf16 d=128 forward of packed rows runs 64 queries per
@@ -235,8 +245,8 @@ def test_fwd_step_partial(case):
     assert np.all(on[np.transpose(dead, (0, 2, 1))] == 0)
 
 
-@pytest.mark.parametrize("case", STEP_CASES + WIDE_BWD_CASES + LONG_SEG_CASES + WIDE_LONG_SEG_CASES[1:],
-                         ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case", STEP_CASES + WIDE_BWD_CASES + SHORT_WALK_BWD_CASES + LONG_SEG_CASES +
+                         WIDE_LONG_SEG_CASES[1:], ids=lambda c: "-".join(map(str, c)))
 def test_bwd_step(case):
     """One backward step with the oracle's own final LSE/delta as inputs: dQ, dK, dV."""
     ra = lib()
