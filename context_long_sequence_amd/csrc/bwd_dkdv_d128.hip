@@ -261,11 +261,10 @@ __global__ __launch_bounds__(64 * NW) void dkdv_d128_kernel(BwdArgs a) {
   // The LSE row of a tile is used as -LSE * log2(e) (the exponent of P in base 2).
   // Wave 0, which copied it, rescales it in place one step before the tile is
   // used: it reads the row at the start of step t (after waiting for its copy of
-  // tile t+1's row, which precedes the 8 row-block copies of that tile and the 9 of
-  // tile t+2) and writes it back after step t's arithmetic; the barrier of step t+1
-  // publishes it.  Saves 32 multiplications per lane and tile in the other waves.
+  // tile t+1's row, which precedes that tile's 8 row-block copies and tile t+2's
+  // row, if any) and writes it back after step t's arithmetic; the barrier of step
+  // t+1 publishes it.  Saves 32 multiplications per lane and tile in the other waves.
   auto rescale_wait = [&](bool next2) {
-    // Tile it+1's row was followed by its 8 row blocks and tile it+2's row (if any).
     if (next2)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
     else
