@@ -336,16 +336,19 @@ __global__ __launch_bounds__(kThreads) void fwd_step_kernel(FwdArgs a) {
 // before the softmax of tile t, so the matrix cores work while the vector ALUs do
 // the softmax.
 // ------------------------------------------------------------------------------------
-constexpr int kD128BN = 32;  // keys per tile
 
 // NW = 4 or 8 waves (x 32 queries) per workgroup: with 8, two waves per SIMD share
 // each K/V tile copy (half the tile traffic per query); 4 keeps more workgroups for
 // small grids.
 template <bool kSeg, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
-  static_assert(NW == 4 || NW == 8, "a 32-row tile is 8 blocks of 1 KiB, split evenly over the waves");
-  constexpr int D = 128, BN = kD128BN, BM = 32 * NW;
-  constexpr int kD128Blocks = 8 / NW;  // 1 KiB blocks of a tile copied by each wave
+  static_assert(NW == 4 || NW == 8, "tile blocks of 1 KiB split evenly over the waves");
+  // 8-wave workgroups take 64-key tiles (two 32-key blocks): half the barriers,
+  // copies and per-tile reductions per key.
+  constexpr int KB = NW == 8 ? 2 : 1;  // 32-key blocks per tile
+  constexpr int D = 128, BN = 32 * KB, BM = 32 * NW;
+  static_assert(!(kSeg && KB > 1), "packed rows use 32-key tiles");
+  constexpr int kD128Blocks = BN / 4 / NW;  // 1 KiB blocks (4 rows) of a tile copied by each wave
   // Each slot its own array, so the compiler can tell the copies in flight from
   // the tiles being read.
   __shared__ __attribute__((aligned(1024))) __bf16 ks0[BN * D];
@@ -477,20 +480,33 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
 
+  struct Scores {
+    f32x16 s[KB];
+  };
   auto qk = [&](const __bf16* kt) {
     const char* base = reinterpret_cast<const char*>(kt);
     bf16x8 kf[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) kf[s] = load_bf16x8(base + (kA ^ (s << 5)));
     __builtin_amdgcn_sched_barrier(0);  // all eight reads in flight before the first MFMA
-    f32x16 acc = f32x16{};
+    Scores acc;
+    acc.s[0] = f32x16{};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc = mfma_bf16(kf[s], qf[s], acc);
+    for (int s = 0; s < 8; ++s) acc.s[0] = mfma_bf16(kf[s], qf[s], acc.s[0]);
+    if constexpr (KB > 1) {
+      // Block 1 (keys 32..63, 8 KiB further): its operands reuse the registers as
+      // block 0's MFMAs release them.
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kf[s] = load_bf16x8(base + 8192 + (kA ^ (s << 5)));
+      acc.s[1] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) acc.s[1] = mfma_bf16(kf[s], qf[s], acc.s[1]);
+    }
     return acc;
   };
 
   // Softmax of tile t's scores and O^T += V^T P^T.
-  auto consume = [&](f32x16 sc, const __bf16* vt, int t) {
+  auto consume = [&](Scores sc, const __bf16* vt, int t) {
     const int k0 = t * BN;
     bool partial = (k0 + BN > a.Sk);
     if (a.causal) partial |= (k0 + BN - 1 > wave_last_visible);
@@ -502,7 +518,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
       partial |= !(sk_lo == sk_hi && sk_lo == seg_w_lo && seg_w_lo == seg_w_hi);
     }
     if (partial) {  // one wave-uniform branch around the element mask
-      // Register i of half h holds key k0 + 16h + i.
+      // Register i of half h of block kb holds key k0 + 32kb + 16h + i.
       const int lim = min(a.causal ? causal_lim - k0 : (1 << 30), a.Sk - 1 - k0 - 16 * half);
       if constexpr (kSeg) {
 #pragma unroll
@@ -511,19 +527,26 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
           const int s_lo = seg_row[a.kv_offset + min(k0 + i, a.Sk - 1)];
           const int s_hi = seg_row[a.kv_offset + min(k0 + 16 + i, a.Sk - 1)];
           const bool vis = (i <= lim) & ((half ? s_hi : s_lo) == seg_q);
-          sc[i] = vis ? sc[i] : -INFINITY;
+          sc.s[0][i] = vis ? sc.s[0][i] : -INFINITY;
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = (i <= lim) ? sc[i] : -INFINITY;
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc.s[kb][i] = (i + 32 * kb <= lim) ? sc.s[kb][i] : -INFINITY;
       }
     }
 
     // Row max and (below) row sum as trees of independent operations, so that the
     // vector instructions between two MFMAs do not wait on one another.
     auto max3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
-    const float r = fmaxf(max3(max3(sc[0], sc[1], sc[2]), max3(sc[3], sc[4], sc[5]), max3(sc[6], sc[7], sc[8])),
-                          max3(max3(sc[9], sc[10], sc[11]), max3(sc[12], sc[13], sc[14]), sc[15]));
+    float r = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const f32x16& c = sc.s[kb];
+      r = fmaxf(r, fmaxf(max3(max3(c[0], c[1], c[2]), max3(c[3], c[4], c[5]), max3(c[6], c[7], c[8])),
+                         max3(max3(c[9], c[10], c[11]), max3(c[12], c[13], c[14]), c[15])));
+    }
     const float tmax = half_max(r) * a.scale_log2;
     // Lazy rescaling: the running max only moves when a row's max grows by more
     // than kFwdSlack (log2 units), so P stays <= 2^kFwdSlack and most tiles skip the
@@ -537,42 +560,45 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
       for (int db = 0; db < 4; ++db) oacc[db] *= al;
     }
     const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
-    float p[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(sc[i], a.scale_log2, neg_m));
-    float ps4[4];
+    for (int kb = 0; kb < KB; ++kb) {
+      float p[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ps4[j] = (p[4 * j] + p[4 * j + 1]) + (p[4 * j + 2] + p[4 * j + 3]);
-    l_run += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
-    const bf16x8 pf0 = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-    const bf16x8 pf1 = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+      for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(sc.s[kb][i], a.scale_log2, neg_m));
+      float ps4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ps4[j] = (p[4 * j] + p[4 * j + 1]) + (p[4 * j + 2] + p[4 * j + 3]);
+      l_run += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+      const bf16x8 pf0 = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      const bf16x8 pf1 = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
 
-    // O^T += V^T P^T: register 8m+j of half h holds key 16h + 8m + j.
-    const char* vb = reinterpret_cast<const char*>(vt);
+      // O^T += V^T P^T: register 8m+j of half h holds key 32kb + 16h + 8m + j.
+      const char* vb = reinterpret_cast<const char*>(vt) + 8192 * kb;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      bf16x8 vf[4];
+      for (int m = 0; m < 2; ++m) {
+        bf16x8 vf[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x4_t x0 = tr_read(vb + (vB0 ^ (db << 6)) + 2048 * m);
-        const bf16x4_t x1 = tr_read(vb + (vB1 ^ (db << 6)) + 2048 * m);
-        vf[db] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        for (int db = 0; db < 4; ++db) {
+          const bf16x4_t x0 = tr_read(vb + (vB0 ^ (db << 6)) + 2048 * m);
+          const bf16x4_t x1 = tr_read(vb + (vB1 ^ (db << 6)) + 2048 * m);
+          vf[db] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        }
+        // Two waves share each SIMD.  With 4-wave workgroups (two per CU) the products
+        // go out at raised priority, ahead of the other wave's softmax instructions
+        // (8K chunk step -2 to -7 %); with 8-wave workgroups each group of four stays
+        // together in the schedule (64K chunk step -1 %), where the priority gained
+        // nothing.
+        if constexpr (NW == 4)
+          __builtin_amdgcn_s_setprio(1);
+        else
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] = mfma_bf16(vf[db], m ? pf1 : pf0, oacc[db]);
+        if constexpr (NW == 4)
+          __builtin_amdgcn_s_setprio(0);
+        else
+          __builtin_amdgcn_sched_barrier(0);
       }
-      // Two waves share each SIMD.  With 4-wave workgroups (two per CU) the products
-      // go out at raised priority, ahead of the other wave's softmax instructions
-      // (8K chunk step -2 to -7 %); with 8-wave workgroups each group of four stays
-      // together in the schedule (64K chunk step -1 %), where the priority gained
-      // nothing.
-      if constexpr (NW == 4)
-        __builtin_amdgcn_s_setprio(1);
-      else
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] = mfma_bf16(vf[db], m ? pf1 : pf0, oacc[db]);
-      if constexpr (NW == 4)
-        __builtin_amdgcn_s_setprio(0);
-      else
-        __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -583,7 +609,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
   // The slots freed by that barrier receive K(t+3) and V(t+2).
   // `steady`: the caller guarantees t + 3 < kt_end, so the waits and copies need no
   // tests (the bulk of the loop); the last steps go through the general form.
-  f32x16 s_next = f32x16{};
+  Scores s_next{};
   auto step = [&](auto steady_tag, int t, const __bf16* kq, const __bf16* vc, __bf16* kn, __bf16* vn) {
     constexpr bool kSteady = decltype(steady_tag)::value;
     if (kSteady || t + 2 < kt_end)
@@ -598,7 +624,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_step_d128_kernel(FwdArgs a) {
     if (kSteady || t + 3 < kt_end) copy_tile(kbase, t + 3, kn);
     if (kSteady || t + 2 < kt_end) copy_tile(vbase, t + 2, vn);
     // Scores of tile t+1 (on the last step the slot is stale and the result unused).
-    const f32x16 sc = s_next;
+    const Scores sc = s_next;
     s_next = qk(kq);
     consume(sc, vc, t);
   };
