@@ -694,10 +694,12 @@ ra_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
     // K/V operand read feeds two MFMAs.  On unpacked rows the 8-wave kernel below,
     // with two waves per SIMD to hide the softmax, is as fast or faster.
     if (args.seg != nullptr && fwd64_d128_workgroups(args) >= 2 * 256) return launch_fwd64_d128(args, stream);
-    // 8-wave workgroups when the grid still gives every CU (256 on MI355X) four of
-    // them and no segment test runs (packed rows keep the finer 128-query tiles).
+    // 8-wave workgroups when the grid still gives every CU (256 on MI355X) two of
+    // them and no segment test runs (packed rows keep the finer 128-query tiles):
+    // 4096-query chunks -2 %; with one per CU (2048-query chunks) the diagonal step
+    // was 5 % slower.
     const int64_t n8 = (int64_t)args.B * args.Hq * ((args.Sq + 255) / 256);
-    const bool wide = args.seg == nullptr && n8 >= 4 * 256;
+    const bool wide = args.seg == nullptr && n8 >= 2 * 256;
     FwdArgs a2 = args;
     a2.n_qtiles = (args.Sq + (wide ? 255 : 127)) / (wide ? 256 : 128);
     const unsigned n2 = (unsigned)((int64_t)args.B * args.Hq * a2.n_qtiles);
