@@ -379,6 +379,8 @@ WIDE_CASES = [
     (1900, 2100, 2100, 0, True),      # earlier chunk: every block fully visible
     (2048, 1500, 900, 1200, True),    # partly in the future: some rows see nothing
     (2000, 333, 0, 0, False),         # non-causal, short chunk
+    (1900, 20, 0, 0, False),          # chunk shorter than one 32-key block of a 64-key tile
+    (2048, 40, 2048, 2030, True),     # 40 keys: the tile's second block partly past the chunk end
 ]
 
 
